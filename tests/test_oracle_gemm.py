@@ -1,0 +1,183 @@
+"""Pins of the oracle's contraction and epilogues.
+
+The integer contraction has a plain definition (sum_k q[m,k] * w[n,k]), so it is
+checked against numpy's int64 matmul and closed forms.  The epilogue (scales +
+bias fused after the integer GEMM, "CLEF Calibrated INT8 ConvRot" card,
+Benefits list) and the paired gate/up SwiGLU ("Loading CLEF INT8": gate/up
+packed into one weight at load time, fuse_mlp) are checked against exact
+rational arithmetic and scipy's logistic function; the whole int8 path is
+checked against the unquantized fp64 product through an a-priori error bound.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit
+
+import workloads as W
+
+
+def _bf16_values():
+    codes = torch.arange(0, 0x7F80, dtype=torch.int32).to(torch.int16)
+    return codes.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+BF16 = _bf16_values()
+
+
+def _nearest_bf16_fraction(v: Fraction) -> int:
+    """Nearest bf16 code to an exact rational (ties to even), by comparison with neighbours."""
+    mag = abs(v)
+    j = int(np.searchsorted(BF16, float(mag)))
+    best, bestd = None, None
+    for c in range(max(0, j - 2), min(len(BF16), j + 2)):
+        d = abs(Fraction(float(BF16[c])) - mag)
+        if bestd is None or d < bestd or (d == bestd and c % 2 == 0):
+            best, bestd = c, d
+    return best | (0x8000 if v < 0 else 0)
+
+
+def _bf16_to_f64(bits):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 1, 64), (7, 5, 192), (33, 17, 1024), (298, 64, 1024)])
+def test_gemm_i32_matches_numpy(orc, M, N, K):
+    q = W.random_codes((M, K), seed=M * 7 + K).numpy()
+    w = W.random_codes((N, K), seed=N * 11 + K).numpy()
+    ref = q.astype(np.int64) @ w.astype(np.int64).T
+    assert np.array_equal(orc.gemm_i32(q, w), ref.astype(np.int32))
+
+
+def test_gemm_i32_closed_forms(orc):
+    K = 17408
+    q = np.full((2, K), 127, dtype=np.int8)
+    q[1] = -127
+    w = np.full((3, K), -127, dtype=np.int8)
+    w[1] = 127
+    w[2] = 0
+    w[2, 5] = 1                          # one-hot column picks q[:, 5]
+    acc = orc.gemm_i32(q, w)
+    assert acc[0, 0] == -16129 * K and acc[1, 0] == 16129 * K
+    assert acc[0, 1] == 16129 * K and acc[1, 1] == -16129 * K
+    assert acc[0, 2] == 127 and acc[1, 2] == -127
+    big = 131072                         # largest K whose worst case still fits int32
+    a = orc.gemm_i32(np.full((1, big), -127, np.int8), np.full((1, big), -127, np.int8))
+    assert a[0, 0] == 16129 * big < 2 ** 31
+
+
+def test_gemm_fp8_is_exact(orc):
+    g = np.random.default_rng(41)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    q = g.choice(codes, (9, 512)).astype(np.uint8)
+    w = g.choice(codes, (6, 512)).astype(np.uint8)
+    dq = torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    dw = torch.from_numpy(w).view(torch.float8_e4m3fn).double().numpy()
+    # products have <= 8 significant bits in [2^-18, 2^17]; their fp64 sums are exact
+    assert np.array_equal(orc.gemm_fp8(q, w), dq @ dw.T)
+
+
+def test_dequant_unit_scales_is_bf16_of_acc(orc):
+    q = W.random_codes((5, 256), seed=42).numpy()
+    w = W.random_codes((7, 256), seed=43).numpy()
+    ones_m = np.ones(5, np.float32)
+    ones_n = np.ones(7, np.float32)
+    y = orc.gemm_dequant(q, ones_m, w, ones_n, None)
+    acc = q.astype(np.int64) @ w.astype(np.int64).T
+    want = np.array([[_nearest_bf16_fraction(Fraction(int(a))) for a in row] for row in acc], np.uint16)
+    assert np.array_equal(y, want)
+
+
+def test_dequant_exact_rational(orc):
+    M, N, K = 6, 40, 320
+    q = W.random_codes((M, K), seed=44).numpy()
+    w = W.random_codes((N, K), seed=45).numpy()
+    s_tok = W.random_scales(M, seed=46).numpy()
+    s_ch = W.random_scales(N, seed=47, lo=1e-5, hi=1e-3).numpy()
+    bias = W.bits((torch.randn(N, generator=torch.Generator().manual_seed(48)) * 0.01).to(torch.bfloat16))
+    y = orc.gemm_dequant(q, s_tok, w, s_ch, bias)
+    acc = q.astype(np.int64) @ w.astype(np.int64).T
+    b = _bf16_to_f64(bias)
+    for m in range(M):
+        for n in range(N):
+            v = Fraction(int(acc[m, n])) * Fraction(float(s_tok[m])) * Fraction(float(s_ch[n])) + Fraction(float(b[n]))
+            assert int(y[m, n]) == _nearest_bf16_fraction(v), (m, n)
+    # bias is added to every row: the NULL-bias result differs exactly by it before rounding
+    y0 = orc.gemm_dequant(q, s_tok, w, s_ch, None)
+    assert not np.array_equal(y0, y)
+
+
+def test_swiglu_packing_and_values(orc):
+    M, N, K = 5, 24, 256
+    q = W.random_codes((M, K), seed=51).numpy()
+    w = W.random_codes((2 * N, K), seed=52).numpy()
+    w[3] = 0                              # gate row 3 is zero: silu(0) * u = 0
+    s_tok = W.random_scales(M, seed=53).numpy()
+    s_ch = W.random_scales(2 * N, seed=54, lo=1e-4, hi=1e-3).numpy()
+    bias = W.bits((torch.randn(2 * N, generator=torch.Generator().manual_seed(55)) * 0.05).to(torch.bfloat16))
+    bias[3] = 0
+    y = orc.gemm_swiglu(q, s_tok, w, s_ch, bias)
+    assert y.shape == (M, N)
+    acc = q.astype(np.int64) @ w.astype(np.int64).T
+    b = _bf16_to_f64(bias)
+    vals = acc * s_tok[:, None].astype(np.float64) * s_ch[None, :].astype(np.float64) + b[None, :]
+    g, u = vals[:, :N], vals[:, N:]
+    ref = g * expit(g) * u                # gate = first half of the packed rows
+    got = _bf16_to_f64(y)
+    assert np.all((y[:, 3] & 0x7FFF) == 0)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-30))) - 7)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-9))
+    swapped = u * expit(u) * g            # a transposed packing would give this
+    assert not np.allclose(got, swapped, rtol=1e-2)
+
+
+def test_silu_limits(orc):
+    K = 64
+    q = np.ones((1, K), dtype=np.int8)
+    w = np.zeros((4, K), dtype=np.int8)
+    w[0] = 100                            # gate 0: large positive; up 0 (row 2) = 1
+    w[1] = -100                           # gate 1: large negative
+    w[2] = 1
+    w[3] = 1
+    s_tok = np.ones(1, np.float32)
+    s_ch = np.array([1.0, 1.0, 0.5, 0.5], np.float32)
+    y = _bf16_to_f64(orc.gemm_swiglu(q, s_tok, w, s_ch, None))
+    assert y[0, 0] == 6400.0 * 32.0        # silu(6400) = 6400 in fp64; times up = 32
+    assert y[0, 1] == 0.0 and np.signbit(y[0, 1])   # silu(-6400) = -0 (underflow), times 32
+
+
+def test_linear_is_quantize_then_gemm_dequant(orc):
+    wl = W.custom("linear", 40, 512, 72, 128, seed=56)
+    inp = W.make_inputs(wl)
+    x, w, bias = W.bits(inp.x), W.bits(inp.w), W.bits(inp.bias)
+    wq, s_ch = orc.quantize_i8(w, 128)
+    q, s_tok = orc.quantize_i8(x, 128)
+    assert np.array_equal(orc.linear(x, wq, s_ch, bias, 128), orc.gemm_dequant(q, s_tok, wq, s_ch, bias))
+    wqf, s_chf = orc.quantize_fp8(w, 128)
+    qf, s_tokf = orc.quantize_fp8(x, 128)
+    assert np.array_equal(orc.fp8_linear(x, wqf, s_chf, bias, 128),
+                          orc.fp8_gemm_dequant(qf, s_tokf, wqf, s_chf, bias))
+    wg = W.bits(torch.cat([inp.w, inp.w.flip(0)]))
+    wgq, s_g = orc.quantize_i8(wg, 128)
+    assert np.array_equal(orc.gateup_swiglu(x, wgq, s_g, None, 128), orc.gemm_swiglu(q, s_tok, wgq, s_g, None))
+
+
+def test_linear_error_bound_against_unquantized(orc):
+    """|y_q - (x W^T + b)| <= s_tok/2 sum|W| + s_ch/2 sum|x| + K s_tok s_ch / 4 + bf16 half-ulp."""
+    wl = W.WORKLOADS["short_298x1024x1024"]
+    inp = W.make_inputs(wl)
+    x, w, bias = W.bits(inp.x), W.bits(inp.w), W.bits(inp.bias)
+    wq, s_ch = orc.quantize_i8(w)
+    q, s_tok = orc.quantize_i8(x)
+    y = _bf16_to_f64(orc.linear(x, wq, s_ch, bias))
+    xf, wf, bf = inp.x.double().numpy(), inp.w.double().numpy(), inp.bias.double().numpy()
+    exact = xf @ wf.T + bf
+    bound = (s_tok[:, None] / 2 * np.abs(wf).sum(1)[None, :] * (1 + 2.0 ** -16)
+             + s_ch[None, :] / 2 * np.abs(xf).sum(1)[:, None] * (1 + 2.0 ** -16)
+             + wl.K * s_tok[:, None] * s_ch[None, :] / 4
+             + np.abs(y) * 2.0 ** -8)
+    assert np.all(np.abs(y - exact) <= bound)
+    # and the error is a small fraction of the output scale (the method is usable)
+    rel = np.linalg.norm(y - exact) / np.linalg.norm(exact)
+    assert rel < 0.05
