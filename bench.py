@@ -1,0 +1,201 @@
+"""Benchmark of the W8A8 quantized projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step is one pass of the whole hot path over one batch: the per-token
+quantizer (stage 1) followed by the int8 GEMM with its fused epilogue (stages 2
+and 3) -- the two kernels ``w8a8_linear`` / ``w8a8_gateup_swiglu`` /
+``w8a8_fp8_linear`` enqueue, launched here through their stage entry points so
+that each kernel is bracketed by HIP events on the launch stream.  Inputs
+(activations, quantized weights, scales, bias) are resident in HBM before the
+timed region; successive steps rotate through enough copies of them (>= 512 MiB
+in total) that no step finds its operands in the 256 MiB last-level cache.
+
+Prints one JSON line: metric = TOPS of the whole path (2*M*N_w*K ops per step
+over the step time), the roofline of the dominant kernel (the GEMM) with its
+event-timed average duration, the quantizer's bandwidth, and the CPU oracle
+timed on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+DEFAULT_WORKLOAD = "rot_1502x4096x4096"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_FP8_TFLOPS = 5000.0     # dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0        # HBM3E 8 TB/s
+ROTATION_BYTES = 512 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def kernel_sources_digest() -> str:
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "quantize.hip", "internal.h"):
+        h.update((ROOT / "w8a8_quantized_linear_amd" / "csrc" / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources; else None."""
+    p = ROOT / "profiles" / f"traffic_{workload}.json"
+    if not p.exists():
+        return None
+    rec = json.loads(p.read_text())
+    if rec.get("sources_digest") != kernel_sources_digest():
+        return None
+    return rec.get("gemm_bytes_per_launch")
+
+
+def cpu_baseline(wl, inp):
+    """The CPU oracle, as it stands, on the whole workload (all rows), on this host."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    threads = oracle.default_threads()
+    x, w = W.bits(inp.x), W.bits(inp.w)
+    bias = None if inp.bias is None else W.bits(inp.bias)
+    fp8 = wl.kind == "fp8"
+    wq, s_ch = (oracle.quantize_fp8 if fp8 else oracle.quantize_i8)(w, wl.rot_block, threads)
+    # bounded sample: all rows when the whole pass is cheap enough, else a row slice
+    rows = wl.M if wl.M * wl.n_w * wl.K <= 60 * 10 ** 9 else max(1, int(60 * 10 ** 9 // (wl.n_w * wl.K)))
+    xs = np.ascontiguousarray(x[:rows])
+    fn = {"linear": oracle.linear, "gateup": oracle.gateup_swiglu, "fp8": oracle.fp8_linear}[wl.kind]
+    t0 = time.perf_counter()
+    fn(xs, wq, s_ch, bias, wl.rot_block, threads)
+    dt = time.perf_counter() - t0
+    ops = 2 * rows * wl.n_w * wl.K
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} of {wl.M} token rows, one pass (quantize + GEMM + epilogue), "
+                      f"{dt:.2f} s wall on {threads} threads"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the projection shards by token rows with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workloads as W
+    import w8a8_quantized_linear_amd as lib
+
+    wl = W.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    inp = W.make_inputs(wl)
+    fp8 = wl.kind == "fp8"
+    quant = lib.w8a8_quantize_act_fp8 if fp8 else lib.w8a8_quantize_act
+    M, K, Nw = wl.M, wl.K, wl.n_w
+    n_out = wl.N
+
+    # resident operands, several copies so that consecutive steps do not hit in cache
+    x0 = inp.x.to(dev)
+    wq0, s_ch0 = quant(inp.w.to(dev), wl.rot_block)
+    bias0 = None if inp.bias is None else inp.bias.to(dev)
+    per_copy = M * K * 2 + Nw * K + M * K + M * n_out * 2 + 4 * (M + Nw)
+    copies = max(2, -(-ROTATION_BYTES // per_copy))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
+    qs = [torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=dev) for _ in range(copies)]
+    ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(copies)]
+    ys = [torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    torch.cuda.synchronize()
+
+    L = lib._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    qfn = L.w8a8_quantize_act_fp8 if fp8 else L.w8a8_quantize_act
+    gfn = {"linear": L.w8a8_gemm_dequant, "gateup": L.w8a8_gemm_swiglu, "fp8": L.w8a8_fp8_gemm_dequant}[wl.kind]
+    bptr = None if bias0 is None else bias0.data_ptr()
+    sch = s_ch0.data_ptr()
+    qargs = [(xs[i].data_ptr(), M, K, wl.rot_block, qs[i].data_ptr(), ss[i].data_ptr(), stream)
+             for i in range(copies)]
+    gargs = [(qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(),
+              M, n_out, K, stream) for i in range(copies)]
+
+    def step(i, evs=None):
+        c = i % copies
+        if evs is not None:
+            evs[0].record()
+        st = qfn(*qargs[c])
+        if evs is not None:
+            evs[1].record()
+        st |= gfn(*gargs[c])
+        if evs is not None:
+            evs[2].record()
+        if st:
+            raise RuntimeError(f"library call failed with status {st}")
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    tq = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3   # s per quantizer launch
+    tg = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3   # s per GEMM launch
+    ms_per_step = wall / args.steps * 1e3
+    ops = 2 * M * Nw * K
+    q_bytes = 2 * M * K + M * K + 4 * M                      # read bf16 x, write codes + scales
+    g_bytes = M * K + Nw * K + 4 * (M + Nw) + M * n_out * 2 + (0 if bias0 is None else 2 * Nw)
+    peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
+    traffic = stored_traffic(wl.name)
+
+    out = {
+        "metric": "W8A8 linear TOPS incl. quant+dequant, % int8 MFMA peak; quantizer GB/s",
+        "value": ops / (ms_per_step * 1e-3) / 1e12,
+        "unit": "TOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3" if fp8 else "i8",
+        "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": {"workload": wl.name, "M": M, "K": K, "N": n_out, "weight_rows": Nw,
+                   "rot_block": wl.rot_block, "path": wl.kind, "parallelism": "single GPU",
+                   "operand_copies": copies},
+        "pct_of_peak": 100.0 * ops / (ms_per_step * 1e-3) / (peak * 1e12),
+        "roofline": {"bound": "mfma", "achieved": ops / tg / 1e12, "peak": peak, "unit": "TFLOP/s",
+                     "frac": ops / tg / 1e12 / peak, "traffic": traffic,
+                     "kernel": "gemm_tile (GEMM + fused epilogue)", "avg_launch_us": tg * 1e6,
+                     "algorithmic_bytes": g_bytes},
+        "quantizer": {"bound": "hbm", "achieved": q_bytes / tq / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": q_bytes / tq / 1e9 / PEAK_HBM_GBS, "avg_launch_us": tq * 1e6,
+                      "algorithmic_bytes": q_bytes},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -246,12 +246,29 @@ int64_t dot_i8(const int8_t* a, const int8_t* b, int64_t K) {
 // fp8 dot product, exact: every E4M3FN value times 2^9 is an integer of at
 // most 448 * 512 = 229376, so the products times 2^18 are integers below 2^36
 // and their int64 sum is exact for K <= 2^17.
+// The 256 codes' values times 2^9, decoded once (NaN codes marked by a flag).
+struct ScaledE4M3 {
+  int64_t v[256];
+  bool nan[256];
+  ScaledE4M3() {
+    for (int c = 0; c < 256; ++c) {
+      double d = e4m3_decode((uint8_t)c);
+      nan[c] = std::isnan(d);
+      v[c] = nan[c] ? 0 : (int64_t)std::ldexp(d, 9);
+    }
+  }
+};
+const ScaledE4M3& scaled_e4m3() {
+  static const ScaledE4M3 table;
+  return table;
+}
+
 int64_t dot_fp8_scaled(const uint8_t* a, const uint8_t* b, int64_t K) {
+  const ScaledE4M3& t = scaled_e4m3();
   int64_t acc = 0;
   for (int64_t k = 0; k < K; ++k) {
-    double da = e4m3_decode(a[k]), db = e4m3_decode(b[k]);
-    require(!std::isnan(da) && !std::isnan(db), "no fp8 NaN codes");
-    acc += (int64_t)std::ldexp(da, 9) * (int64_t)std::ldexp(db, 9);
+    require(!t.nan[a[k]] && !t.nan[b[k]], "no fp8 NaN codes");
+    acc += t.v[a[k]] * t.v[b[k]];
   }
   return acc;
 }

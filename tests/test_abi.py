@@ -1,0 +1,137 @@
+"""Host-side tests of the C-ABI library: it loads, exports every entry point the
+header declares, and rejects bad arguments before touching any device.
+
+No kernel is launched here.  Argument checks run before the device check, so
+the expected statuses come back on a machine without a GPU; pointers passed
+are dummy, never dereferenced.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+HEADER = ROOT / "include" / "w8a8.h"
+LIB = ROOT / "w8a8_quantized_linear_amd" / "libw8a8.so"
+
+OK, NULLP, SHAPE, MISALIGNED, BADARG, DEVICE = 0, 1, 2, 3, 4, 5
+A = 0x10000   # a 16-byte aligned dummy address (never dereferenced)
+U = A + 8     # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not LIB.exists():
+        from w8a8_quantized_linear_amd import build as b
+        b.build()
+    lib = ctypes.CDLL(str(LIB))
+    P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "w8a8_status_string": (ctypes.c_char_p, [I]),
+        "w8a8_workspace_bytes": (SZ, [I64, I64]),
+        "w8a8_quantize_act": (I, [P, I64, I64, I, P, P, P]),
+        "w8a8_quantize_act_fp8": (I, [P, I64, I64, I, P, P, P]),
+        "w8a8_gemm_i32": (I, [P, P, P, I64, I64, I64, P]),
+        "w8a8_gemm_dequant": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_gemm_swiglu": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_fp8_gemm_dequant": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_linear": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+        "w8a8_gateup_swiglu": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+        "w8a8_fp8_linear": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+def declared_symbols():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w8a8_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_documented_entry_points():
+    want = {"w8a8_status_string", "w8a8_workspace_bytes", "w8a8_quantize_act",
+            "w8a8_quantize_act_fp8", "w8a8_gemm_i32", "w8a8_gemm_dequant", "w8a8_gemm_swiglu",
+            "w8a8_fp8_gemm_dequant", "w8a8_linear", "w8a8_gateup_swiglu", "w8a8_fp8_linear"}
+    assert want <= set(declared_symbols())
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(7):
+        assert lib.w8a8_status_string(s).decode().startswith("W8A8_")
+    assert b"unknown" in lib.w8a8_status_string(99)
+
+
+def test_workspace_bytes(lib):
+    assert lib.w8a8_workspace_bytes(0, 128) == 0
+    assert lib.w8a8_workspace_bytes(1, 128) == 256 + 256
+    assert lib.w8a8_workspace_bytes(12016, 17408) == 12016 * 17408 + ((12016 * 4 + 255) // 256) * 256
+    assert lib.w8a8_workspace_bytes(3, 16) % 256 == 0
+
+
+def test_quantize_argument_checks(lib):
+    q = lib.w8a8_quantize_act
+    assert q(None, 4, 128, 0, A, A, None) == NULLP
+    assert q(A, 4, 128, 0, None, A, None) == NULLP
+    assert q(A, 4, 128, 0, A, None, None) == NULLP
+    assert q(A, -1, 128, 0, A, A, None) == SHAPE
+    assert q(A, 4, 0, 0, A, A, None) == SHAPE
+    assert q(A, 4, 24, 0, A, A, None) == SHAPE               # K % 16
+    assert q(A, 4, 131072 + 16, 0, A, A, None) == SHAPE      # K > max
+    assert q(A, 4, 64, 128, A, A, None) == SHAPE             # rotation needs K % 128
+    assert q(A, 4, 128, 64, A, A, None) == BADARG            # rot_block not 0/128
+    assert q(U, 4, 128, 0, A, A, None) == MISALIGNED
+    assert q(A, 4, 128, 0, U, A, None) == MISALIGNED
+    assert q(A, 0, 128, 0, A, A, None) == OK                 # M == 0: nothing enqueued
+    assert lib.w8a8_quantize_act_fp8(A, 0, 256, 128, A, A, None) == OK
+    assert lib.w8a8_quantize_act_fp8(A, 4, 200, 128, A, A, None) == SHAPE
+
+
+def test_gemm_argument_checks(lib):
+    g = lib.w8a8_gemm_dequant
+    assert g(None, A, A, A, None, A, 4, 8, 128, None) == NULLP
+    assert g(A, None, A, A, None, A, 4, 8, 128, None) == NULLP
+    assert g(A, A, A, None, None, A, 4, 8, 128, None) == NULLP
+    assert g(A, A, A, A, None, None, 4, 8, 128, None) == NULLP
+    assert g(A, A, A, A, None, A, 4, 8, 64, None) == SHAPE    # K % 128
+    assert g(A, A, A, A, None, A, 4, 12, 128, None) == SHAPE  # N % 8
+    assert g(A, A, A, A, None, A, 4, 0, 128, None) == SHAPE
+    assert g(A, A, A, A, None, A, -2, 8, 128, None) == SHAPE
+    assert g(A, A, A, A, None, A, 4, 8, 131072 + 128, None) == SHAPE
+    assert g(A, A, A, A, U, A, 4, 8, 128, None) == MISALIGNED  # bias
+    assert g(A, A, U, A, None, A, 4, 8, 128, None) == MISALIGNED
+    assert g(A, A, A, A, None, A, 0, 8, 128, None) == OK
+    assert lib.w8a8_gemm_i32(A, A, None, 4, 8, 128, None) == NULLP
+    assert lib.w8a8_gemm_i32(A, A, A, 0, 8, 128, None) == OK
+    assert lib.w8a8_gemm_swiglu(A, A, A, A, None, A, 4, 8, 100, None) == SHAPE
+    assert lib.w8a8_fp8_gemm_dequant(A, A, A, A, None, A, 4, 8, 256, None) in (OK, DEVICE)
+
+
+def test_whole_path_argument_checks(lib):
+    f = lib.w8a8_linear
+    ws = lib.w8a8_workspace_bytes(4, 256)
+    assert f(A, A, A, None, A, 4, 8, 256, 0, None, ws, None) == NULLP
+    assert f(None, None, None, None, None, 0, 8, 256, 0, None, 0, None) == OK  # M == 0 reads nothing
+    assert f(A, A, A, None, A, 4, 8, 256, 0, A, ws - 1, None) == BADARG   # workspace too small
+    assert f(A, A, A, None, A, 4, 8, 256, 3, A, ws, None) == BADARG      # rot_block
+    assert f(A, A, A, None, A, 4, 8, 192, 0, A, ws, None) == SHAPE       # K % 128
+    assert f(A, A, A, None, A, 4, 8, 256, 0, U, ws, None) == MISALIGNED
+    assert f(A, A, A, None, A, 0, 8, 256, 0, A, 0, None) == OK
+    assert lib.w8a8_gateup_swiglu(A, A, A, None, A, 4, 8, 256, 128, A, ws - 256, None) == BADARG
+    assert lib.w8a8_fp8_linear(A, A, None, None, A, 4, 8, 256, 0, A, ws, None) == NULLP
+
+
+def test_valid_call_without_gpu_reports_device(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present; covered by the GPU tests")
+    assert lib.w8a8_quantize_act(A, 4, 128, 0, A, A, None) == DEVICE
+    assert lib.w8a8_gemm_i32(A, A, A, 4, 8, 128, None) == DEVICE

@@ -1,0 +1,131 @@
+"""GPU parity of the whole paths (quantize + GEMM + epilogue) against the CPU oracle.
+
+* Each of the five workloads at its full size, in the launch configuration the
+  benchmark times: the GPU quantizes the weight itself (compared with the
+  oracle's weight codes and scales, whole matrix), runs the whole path, and a
+  seeded sample of token rows (first/last rows, rows on tile boundaries) is
+  recomputed by the oracle one by one: activation codes and scales (read back
+  from the workspace) and every output column of those rows.
+* Smaller shapes compared on every element.
+* Properties that hold at any size: rows are byte-identical however the batch
+  is split (row results must not depend on batching), repeated runs are
+  byte-identical, and a non-default stream gives the same bytes.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import w8a8_quantized_linear_amd as lib
+    return lib
+
+
+def _gpu_path(lib, wl, x, wq, s_ch, bias, workspace=None, out=None):
+    fn = {"linear": lib.w8a8_linear, "gateup": lib.w8a8_gateup_swiglu, "fp8": lib.w8a8_fp8_linear}[wl.kind]
+    return fn(x, wq, s_ch, bias, rot_block=wl.rot_block, workspace=workspace, out=out)
+
+
+def _oracle_quant(orc, wl, a_bits):
+    return orc.quantize_fp8(a_bits, wl.rot_block) if wl.kind == "fp8" else orc.quantize_i8(a_bits, wl.rot_block)
+
+
+def _oracle_epilogue(orc, wl, q, s_tok, wq, s_ch, bias_bits):
+    if wl.kind == "fp8":
+        return orc.fp8_gemm_dequant(q, s_tok, wq, s_ch, bias_bits)
+    if wl.kind == "gateup":
+        return orc.gemm_swiglu(q, s_tok, wq, s_ch, bias_bits)
+    return orc.gemm_dequant(q, s_tok, wq, s_ch, bias_bits)
+
+
+def _check_workload(lib, orc, wl, rows=None):
+    say(f"workload {wl.name}: M={wl.M} K={wl.K} N={wl.N} kind={wl.kind} rot={wl.rot_block}")
+    inp = W.make_inputs(wl)
+    fp8 = wl.kind == "fp8"
+    quant = lib.w8a8_quantize_act_fp8 if fp8 else lib.w8a8_quantize_act
+    compare_codes = compare_codes_fp8 if fp8 else compare_codes_i8
+    dev = torch.device("cuda")
+    x = inp.x.to(dev)
+    bias = None if inp.bias is None else inp.bias.to(dev)
+    wq, s_ch = quant(inp.w.to(dev), wl.rot_block)
+    ws = torch.empty(lib.workspace_bytes(wl.M, wl.K), dtype=torch.uint8, device=dev)
+    y = _gpu_path(lib, wl, x, wq, s_ch, bias, workspace=ws)
+    torch.cuda.synchronize()
+
+    wq_ref, s_ch_ref = _oracle_quant(orc, wl, W.bits(inp.w))
+    compare_codes(wq.cpu().numpy(), wq_ref, "weight codes")
+    assert np.array_equal(s_ch.cpu().numpy().view(np.uint32), s_ch_ref.view(np.uint32)), "weight scales"
+
+    rows = np.arange(wl.M) if rows is None else rows
+    x_rows = W.bits(inp.x)[rows]
+    q_ref, s_ref = _oracle_quant(orc, wl, x_rows)
+    codes = ws[: wl.M * wl.K].view(wl.M, wl.K).cpu().numpy()
+    off = (wl.M * wl.K + 255) // 256 * 256
+    s_tok = ws[off: off + 4 * wl.M].view(torch.float32).cpu().numpy()
+    compare_codes(codes[rows].view(np.uint8 if fp8 else np.int8), q_ref, "activation codes")
+    assert np.array_equal(s_tok[rows].view(np.uint32), s_ref.view(np.uint32)), "activation scales"
+
+    bias_bits = None if inp.bias is None else W.bits(inp.bias)
+    y_ref = _oracle_epilogue(orc, wl, q_ref, s_ref, wq_ref, s_ch_ref, bias_bits)
+    compare_bf16(bf16_bits(y)[rows], y_ref, f"{wl.name} outputs ({len(rows)} rows)")
+
+
+@pytest.mark.parametrize("name", W.ORDER)
+def test_workload_full_size(lib, orc, name):
+    wl = W.WORKLOADS[name]
+    rows = None if wl.M * wl.n_w * wl.K <= 2 ** 30 else sample_rows(wl.M, n=40 if wl.kind != "fp8" else 24,
+                                                                   seed=wl.seed)
+    _check_workload(lib, orc, wl, rows)
+
+
+SMALL = [
+    W.custom("linear", 1, 128, 8, 0, seed=1),
+    W.custom("linear", 129, 256, 136, 128, seed=2),
+    W.custom("linear", 300, 1024, 264, 128, outlier_frac=0.005, outlier_factor=50.0, seed=3),
+    W.custom("linear", 64, 768, 40, 0, bias=False, x_kind="silu_product", sigma_w=0.01, seed=4),
+    W.custom("gateup", 130, 512, 136, 0, bias=False, seed=5),
+    W.custom("gateup", 257, 384, 72, 128, bias=True, seed=6),
+    W.custom("fp8", 200, 512, 128, 0, bias=False, seed=7),
+    W.custom("fp8", 131, 1024, 264, 128, bias=True, seed=8),
+]
+
+
+@pytest.mark.parametrize("wl", SMALL, ids=[w.name for w in SMALL])
+def test_small_shapes_every_element(lib, orc, wl):
+    _check_workload(lib, orc, wl)
+
+
+@pytest.mark.parametrize("kind,rot", [("linear", 128), ("gateup", 0), ("fp8", 0)])
+def test_batch_split_invariance_and_determinism(lib, kind, rot):
+    wl = W.custom(kind, 600, 1024, 264, rot, seed=11)
+    say(f"batch invariance {wl.name}")
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda")
+    quant = lib.w8a8_quantize_act_fp8 if kind == "fp8" else lib.w8a8_quantize_act
+    wq, s_ch = quant(inp.w.to(dev), rot)
+    x = inp.x.to(dev)
+    bias = None if inp.bias is None else inp.bias.to(dev)
+    whole = _gpu_path(lib, wl, x, wq, s_ch, bias)
+    again = _gpu_path(lib, wl, x, wq, s_ch, bias)
+    pieces, r = [], 0
+    for n in (1, 7, 64, 129, 255, 144):
+        pieces.append(_gpu_path(lib, wl, x[r:r + n].contiguous(), wq, s_ch, bias))
+        r += n
+    assert r == wl.M
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        other = _gpu_path(lib, wl, x, wq, s_ch, bias)
+    torch.cuda.synchronize()
+    b = bf16_bits(whole)
+    assert np.array_equal(b, bf16_bits(again)), "repeat run differs"
+    assert np.array_equal(b, bf16_bits(torch.cat(pieces))), "batch split changes row results"
+    assert np.array_equal(b, bf16_bits(other)), "non-default stream differs"

@@ -1,0 +1,186 @@
+"""GPU parity of each stage against the CPU oracle, through the C ABI.
+
+Stage 1 (quantizer): codes and scales bit-exact (flip budget 1e-4 of one step).
+Stage 2 (integer GEMM, fed identical int8 codes): int32 bit-exact.
+Stage 3 (epilogues, fed identical codes and scales): bf16 within the
+tolerances in tests/parity.py.  Shapes span several 128-wide tiles with ragged
+tails in M and N, the smallest legal shapes, and the largest K.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as W
+from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a HIP device")
+    import w8a8_quantized_linear_amd as lib  # raises if the HIP library is not built
+    return lib
+
+
+def _x_case(M, K, rot, seed, zero_rows=()):
+    wl = W.custom("linear", M, K, 8, rot, outlier_frac=0.01, outlier_factor=30.0, seed=seed)
+    x = W.make_inputs(wl).x.clone()
+    for r in zero_rows:
+        if r < M:
+            x[r] = 0
+    return x
+
+
+QUANT_CASES = [
+    (298, 1024, 0), (1, 16, 0), (7, 48, 0), (5, 5120, 0), (3, 17408, 0), (2, 131072, 0),
+    (300, 1024, 128), (64, 4096, 128), (9, 17408, 128), (2, 131072, 128), (5, 5120, 128),
+]
+
+
+@pytest.mark.parametrize("M,K,rot", QUANT_CASES)
+def test_quantize_int8(lib, orc, M, K, rot):
+    say(f"quantize int8 M={M} K={K} rot={rot}")
+    x = _x_case(M, K, rot, seed=100 + M + K, zero_rows=(1,))
+    q, s = lib.w8a8_quantize_act(x.cuda(), rot)
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_i8(W.bits(x), rot)
+    compare_codes_i8(q.cpu().numpy(), q_ref, "codes")
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("M,K,rot", [(298, 1024, 0), (3, 48, 0), (4, 17408, 0), (33, 4096, 128),
+                                     (3, 17408, 128), (2, 131072, 0)])
+def test_quantize_fp8(lib, orc, M, K, rot):
+    say(f"quantize fp8 M={M} K={K} rot={rot}")
+    x = _x_case(M, K, rot, seed=200 + M + K, zero_rows=(1,))
+    q, s = lib.w8a8_quantize_act_fp8(x.cuda(), rot)
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_fp8(W.bits(x), rot)
+    compare_codes_fp8(q.cpu().numpy(), q_ref, "fp8 codes")
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+
+
+def test_fp8_converter_on_every_bf16_value(lib, orc):
+    """Row amax 448 gives s = 1 exactly, so the codes are the converter's RNE of every input."""
+    vals = torch.arange(0, 65536, dtype=torch.int32).to(torch.int16).view(torch.bfloat16)
+    vals = vals[torch.isfinite(vals.float()) & (vals.float().abs() < 448)]
+    n = (vals.numel() // 127) * 127
+    body = vals[:n].reshape(-1, 127)
+    x = torch.cat([body, torch.full((body.shape[0], 1), 448.0, dtype=torch.bfloat16)], dim=1)
+    x = x.contiguous()  # K = 128
+    say(f"fp8 converter sweep over {n} bf16 values")
+    q, s = lib.w8a8_quantize_act_fp8(x.cuda(), 0)
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_fp8(W.bits(x), 0)
+    assert np.all(s_ref == 1.0)
+    assert np.array_equal(orc.e4m3_decode(q.cpu().numpy()), orc.e4m3_decode(q_ref))
+
+
+GEMM_SHAPES = [(1, 8, 128), (130, 136, 256), (298, 1024, 1024), (257, 264, 384), (64, 8, 17408)]
+
+
+@pytest.mark.parametrize("M,N,K", GEMM_SHAPES)
+def test_gemm_i32_exact(lib, orc, M, N, K):
+    say(f"gemm_i32 M={M} N={N} K={K}")
+    q = W.random_codes((M, K), seed=M + 3 * K)
+    w = W.random_codes((N, K), seed=N + 5 * K)
+    acc = lib.w8a8_gemm_i32(q.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ref = orc.gemm_i32(q.numpy(), w.numpy())
+    assert np.array_equal(acc.cpu().numpy(), ref)
+
+
+def test_gemm_i32_extremes(lib, orc):
+    K = 131072
+    say(f"gemm_i32 extreme codes K={K}")
+    q = torch.full((3, K), 127, dtype=torch.int8)
+    q[1] = -127
+    q[2, ::2] = -127
+    w = torch.full((8, K), -127, dtype=torch.int8)
+    w[1] = 127
+    acc = lib.w8a8_gemm_i32(q.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(acc.cpu().numpy(), orc.gemm_i32(q.numpy(), w.numpy()))
+    assert int(acc[0, 0]) == -16129 * K
+
+
+def _scales_bias(M, Nw, seed, bias=True):
+    s_tok = W.random_scales(M, seed=seed)
+    s_ch = W.random_scales(Nw, seed=seed + 1, lo=1e-5, hi=1e-3)
+    b = ((torch.randn(Nw, generator=torch.Generator().manual_seed(seed + 2)) * 0.01).to(torch.bfloat16)
+         if bias else None)
+    return s_tok, s_ch, b
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(1, 8, 128, True), (130, 136, 256, False),
+                                        (298, 1024, 1024, True), (257, 264, 384, True)])
+def test_gemm_dequant(lib, orc, M, N, K, bias):
+    say(f"gemm_dequant M={M} N={N} K={K} bias={bias}")
+    q = W.random_codes((M, K), seed=11 + M)
+    w = W.random_codes((N, K), seed=13 + N)
+    s_tok, s_ch, b = _scales_bias(M, N, 17, bias)
+    y = lib.w8a8_gemm_dequant(q.cuda(), s_tok.cuda(), w.cuda(), s_ch.cuda(), None if b is None else b.cuda())
+    torch.cuda.synchronize()
+    ref = orc.gemm_dequant(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), None if b is None else W.bits(b))
+    compare_bf16(bf16_bits(y), ref, "y")
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(1, 8, 128, False), (130, 72, 256, True),
+                                        (298, 512, 1024, False), (200, 200, 384, True)])
+def test_gemm_swiglu(lib, orc, M, N, K, bias):
+    say(f"gemm_swiglu M={M} N={N} K={K} bias={bias}")
+    q = W.random_codes((M, K), seed=21 + M)
+    w = W.random_codes((2 * N, K), seed=23 + N)
+    s_tok, s_ch, b = _scales_bias(M, 2 * N, 27, bias)
+    y = lib.w8a8_gemm_swiglu(q.cuda(), s_tok.cuda(), w.cuda(), s_ch.cuda(), None if b is None else b.cuda())
+    torch.cuda.synchronize()
+    ref = orc.gemm_swiglu(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), None if b is None else W.bits(b))
+    compare_bf16(bf16_bits(y), ref, "y")
+
+
+def _fp8_codes(shape, seed):
+    g = torch.Generator().manual_seed(seed)
+    c = torch.randint(0, 256, shape, generator=g, dtype=torch.int32).to(torch.uint8)
+    return torch.where((c & 0x7F) == 0x7F, c ^ 0x01, c)  # no NaN codes
+
+
+@pytest.mark.parametrize("M,N,K,bias", [(1, 8, 128, True), (130, 136, 256, False),
+                                        (298, 1024, 1024, True), (64, 16, 4096, False)])
+def test_fp8_gemm_dequant(lib, orc, M, N, K, bias):
+    say(f"fp8_gemm_dequant M={M} N={N} K={K} bias={bias}")
+    q = _fp8_codes((M, K), 31 + M)
+    w = _fp8_codes((N, K), 37 + N)
+    s_tok, s_ch, b = _scales_bias(M, N, 41, bias)
+    y = lib.w8a8_fp8_gemm_dequant(q.cuda(), s_tok.cuda(), w.cuda(), s_ch.cuda(), None if b is None else b.cuda())
+    torch.cuda.synchronize()
+    ref = orc.fp8_gemm_dequant(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), None if b is None else W.bits(b))
+    compare_bf16(bf16_bits(y), ref, "y")
+
+
+def test_zero_rows_and_empty_batch(lib, orc):
+    say("zero rows / M == 0")
+    x = torch.zeros((3, 256), dtype=torch.bfloat16)
+    x[1, 5] = 2.0
+    q, s = lib.w8a8_quantize_act(x.cuda(), 128)
+    torch.cuda.synchronize()
+    q_ref, s_ref = orc.quantize_i8(W.bits(x), 128)
+    assert np.array_equal(q.cpu().numpy(), q_ref) and np.array_equal(s.cpu().numpy(), s_ref)
+    assert s_ref[0] == 0 and s_ref[2] == 0
+    empty = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    wq = W.random_codes((8, 256), seed=1).cuda()
+    y = lib.w8a8_linear(empty, wq, torch.ones(8, device="cuda"), None, 0)
+    assert y.shape == (0, 8)
+
+
+def test_errors_surface_as_exceptions(lib):
+    say("error statuses")
+    x = torch.zeros((4, 200), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(lib.W8A8Error) as e:
+        lib.w8a8_quantize_act(x, 128)
+    assert e.value.status == 2
+    xb = torch.zeros((4 * 256 + 8,), dtype=torch.bfloat16, device="cuda")[1:1 + 4 * 256].view(4, 256)
+    with pytest.raises(lib.W8A8Error) as e:
+        lib.w8a8_quantize_act(xb, 0)
+    assert e.value.status == 3

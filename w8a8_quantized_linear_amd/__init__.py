@@ -1,0 +1,201 @@
+"""Python binding of the MI355X W8A8 quantized projection library (``libw8a8.so``).
+
+The functions below carry the names of the C entry points declared in
+``include/w8a8.h`` and only marshal arguments: they check dtypes/devices,
+allocate outputs as torch tensors on the current device, pass raw device
+pointers plus ``torch.cuda.current_stream()`` to the C call and turn a non-OK
+status into an exception.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback.  Importing this package without the built
+library raises immediately.
+
+Conventions: bf16 tensors are ``torch.bfloat16``; int8 codes ``torch.int8``;
+E4M3FN codes ``torch.uint8`` (raw codes; view as ``torch.float8_e4m3fn`` if
+desired); scales ``torch.float32``.  All tensors are contiguous, 16-byte
+aligned and on the current CUDA (HIP) device.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional, Tuple
+
+import torch
+
+__all__ = [
+    "LIB_PATH", "W8A8Error", "workspace_bytes",
+    "w8a8_quantize_act", "w8a8_quantize_act_fp8", "w8a8_gemm_i32", "w8a8_gemm_dequant",
+    "w8a8_gemm_swiglu", "w8a8_fp8_gemm_dequant", "w8a8_linear", "w8a8_gateup_swiglu",
+    "w8a8_fp8_linear",
+]
+
+LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
+if not LIB_PATH.exists():
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m w8a8_quantized_linear_amd.build` "
+        "(hipcc, gfx950) first -- there is no non-HIP fallback")
+
+_lib = ctypes.CDLL(str(LIB_PATH))
+_P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+_SIGS = {
+    "w8a8_status_string": (ctypes.c_char_p, [_I]),
+    "w8a8_workspace_bytes": (_SZ, [_I64, _I64]),
+    "w8a8_quantize_act": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "w8a8_quantize_act_fp8": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "w8a8_gemm_i32": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_gemm_dequant": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_gemm_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_fp8_gemm_dequant": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "w8a8_gateup_swiglu": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "w8a8_fp8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+
+class W8A8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {_lib.w8a8_status_string(status).decode()} (status {status})")
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise W8A8Error(status, where)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _want(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int) -> None:
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def workspace_bytes(M: int, K: int) -> int:
+    return int(_lib.w8a8_workspace_bytes(M, K))
+
+
+# ---------------------------------------------------------------- stage 1 ----
+def w8a8_quantize_act(x: torch.Tensor, rot_block: int = 0,
+                      out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Per-row int8 quantizer: x bf16 [M, K] -> (q int8 [M, K], s fp32 [M])."""
+    _want(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    q, s = out if out is not None else (torch.empty((M, K), dtype=torch.int8, device=x.device),
+                                        torch.empty((M,), dtype=torch.float32, device=x.device))
+    _check(_lib.w8a8_quantize_act(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()),
+           "w8a8_quantize_act")
+    return q, s
+
+
+def w8a8_quantize_act_fp8(x: torch.Tensor, rot_block: int = 0,
+                          out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
+    """Per-row E4M3FN quantizer: x bf16 [M, K] -> (codes uint8 [M, K], s fp32 [M])."""
+    _want(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    q, s = out if out is not None else (torch.empty((M, K), dtype=torch.uint8, device=x.device),
+                                        torch.empty((M,), dtype=torch.float32, device=x.device))
+    _check(_lib.w8a8_quantize_act_fp8(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()),
+           "w8a8_quantize_act_fp8")
+    return q, s
+
+
+# ------------------------------------------------------------ stages 2, 3 ----
+def w8a8_gemm_i32(q: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """acc int32 [M, N] = q int8 [M, K] . w int8 [N, K]^T (exact)."""
+    _want(q, torch.int8, "q", 2)
+    _want(w, torch.int8, "w", 2)
+    M, K = q.shape
+    N = w.shape[0]
+    if w.shape[1] != K:
+        raise ValueError("q and w disagree on K")
+    acc = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=q.device)
+    _check(_lib.w8a8_gemm_i32(_ptr(q), _ptr(w), _ptr(acc), M, N, K, _stream()), "w8a8_gemm_i32")
+    return acc
+
+
+def _epi(fname, q, s_tok, w, s_ch, bias, n_out, qdtype, out):
+    _want(q, qdtype, "q", 2)
+    _want(w, qdtype, "w", 2)
+    _want(s_tok, torch.float32, "s_tok", 1)
+    _want(s_ch, torch.float32, "s_ch", 1)
+    if bias is not None:
+        _want(bias, torch.bfloat16, "bias", 1)
+    M, K = q.shape
+    if w.shape[1] != K or s_tok.shape[0] != M or s_ch.shape[0] != w.shape[0]:
+        raise ValueError("inconsistent shapes")
+    if bias is not None and bias.shape[0] != w.shape[0]:
+        raise ValueError("bias length must equal the weight's rows")
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=q.device)
+    _check(getattr(_lib, fname)(_ptr(q), _ptr(s_tok), _ptr(w), _ptr(s_ch), _ptr(bias), _ptr(y),
+                                M, n_out, K, _stream()), fname)
+    return y
+
+
+def w8a8_gemm_dequant(q, s_tok, w, s_ch, bias=None, out=None):
+    """y bf16 [M, N] = (q . w^T) * s_tok * s_ch + bias, from int8 codes."""
+    return _epi("w8a8_gemm_dequant", q, s_tok, w, s_ch, bias, w.shape[0], torch.int8, out)
+
+
+def w8a8_gemm_swiglu(q, s_tok, w_gateup, s_ch, bias=None, out=None):
+    """y bf16 [M, N] = silu(gate) * up over the packed [2N, K] int8 weight."""
+    if w_gateup.shape[0] % 2:
+        raise ValueError("packed gate/up weight needs an even number of rows")
+    return _epi("w8a8_gemm_swiglu", q, s_tok, w_gateup, s_ch, bias, w_gateup.shape[0] // 2,
+                torch.int8, out)
+
+
+def w8a8_fp8_gemm_dequant(q, s_tok, w, s_ch, bias=None, out=None):
+    """y bf16 [M, N] from E4M3FN codes (uint8) with fp32 accumulation."""
+    return _epi("w8a8_fp8_gemm_dequant", q, s_tok, w, s_ch, bias, w.shape[0], torch.uint8, out)
+
+
+# ------------------------------------------------------------ whole paths ----
+def _path(fname, x, w, s_ch, bias, rot_block, n_out, wdtype, workspace, out):
+    _want(x, torch.bfloat16, "x", 2)
+    _want(w, wdtype, "w", 2)
+    _want(s_ch, torch.float32, "s_ch", 1)
+    if bias is not None:
+        _want(bias, torch.bfloat16, "bias", 1)
+    M, K = x.shape
+    if w.shape[1] != K or s_ch.shape[0] != w.shape[0]:
+        raise ValueError("inconsistent shapes")
+    if bias is not None and bias.shape[0] != w.shape[0]:
+        raise ValueError("bias length must equal the weight's rows")
+    need = workspace_bytes(M, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+    _check(getattr(_lib, fname)(_ptr(x), _ptr(w), _ptr(s_ch), _ptr(bias), _ptr(y), M, n_out, K,
+                                rot_block, _ptr(workspace), workspace.numel(), _stream()), fname)
+    return y
+
+
+def w8a8_linear(x, w, s_ch, bias=None, rot_block=0, workspace=None, out=None):
+    """y bf16 [M, N]: per-token int8 quantization of x (optionally rotated), int8 GEMM, dequant."""
+    return _path("w8a8_linear", x, w, s_ch, bias, rot_block, w.shape[0], torch.int8, workspace, out)
+
+
+def w8a8_gateup_swiglu(x, w_gateup, s_ch, bias=None, rot_block=0, workspace=None, out=None):
+    """y bf16 [M, N]: quantize x, int8 GEMM against the packed [2N, K] gate/up weight, SwiGLU."""
+    return _path("w8a8_gateup_swiglu", x, w_gateup, s_ch, bias, rot_block, w_gateup.shape[0] // 2,
+                 torch.int8, workspace, out)
+
+
+def w8a8_fp8_linear(x, w, s_ch, bias=None, rot_block=0, workspace=None, out=None):
+    """y bf16 [M, N]: per-token E4M3FN quantization of x, fp8 GEMM, dequant."""
+    return _path("w8a8_fp8_linear", x, w, s_ch, bias, rot_block, w.shape[0], torch.uint8, workspace, out)
