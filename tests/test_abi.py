@@ -23,8 +23,8 @@ U = A + 8     # misaligned
 @pytest.fixture(scope="module")
 def lib():
     if not LIB.exists():
-        from w8a8_quantized_linear_amd import build as b
-        b.build()
+        import __graft_entry__
+        __graft_entry__._hip_build_module().build()
     lib = ctypes.CDLL(str(LIB))
     P, I64, I, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
     sig = {

@@ -31,7 +31,7 @@ __all__ = [
 LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
 if not LIB_PATH.exists():
     raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m w8a8_quantized_linear_amd.build` "
+        f"{LIB_PATH} is not built; run `python w8a8_quantized_linear_amd/build.py` "
         "(hipcc, gfx950) first -- there is no non-HIP fallback")
 
 _lib = ctypes.CDLL(str(LIB_PATH))

@@ -1,6 +1,8 @@
 """Build ``libw8a8.so`` (the C-ABI library) for gfx950 with hipcc, in-tree.
 
-    python -m w8a8_quantized_linear_amd.build
+    python w8a8_quantized_linear_amd/build.py
+
+(run as a script: importing the package loads the library this produces).
 
 Every HIP source is compiled with packed-fp32 instruction selection disabled
 and the correctly rounded fp32 divide the quantizer relies on.
@@ -35,6 +37,7 @@ COMMON = [
 
 def _compile(src: str) -> Path:
     obj = BUILD_DIR / (src.rsplit(".", 1)[0] + ".o")
+    obj.unlink(missing_ok=True)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
     cmd = [HIPCC, *COMMON, *lang, "-c", str(CSRC / src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -56,6 +59,11 @@ def build() -> Path:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
+    # every kernel launched from host code must have its stub in the library
+    nm = subprocess.run(["nm", "--undefined-only", str(tmp)], capture_output=True, text=True)
+    missing = [l for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError("link produced a library with undefined kernel stubs:\n" + "\n".join(missing))
     os.replace(tmp, LIB)
     return LIB
 

@@ -11,22 +11,33 @@
 //             n and N + n -- the paired gate/up epilogue ("Loading CLEF INT8",
 //             fuse_mlp; gate/up packed into one weight at load time).
 //
-// Design: both operands are K-contiguous ("NT"), so MFMA operands load with no
-// transpose.  A 256-thread workgroup owns a 128 (tokens) x 128 (weight rows)
-// tile; its four waves are arranged 2 x 2 and each accumulates a 64 x 64
-// sub-tile with v_mfma_i32_16x16x64_i8.  E4M3FN operands are widened exactly to
-// bf16 in registers and go through v_mfma_f32_16x16x32_bf16: the gfx950 fp8
-// MFMAs sum groups of products at roughly 14-bit precision (measured: error
-// ~2e-4 of the output rms at K = 4096, whatever the instruction width or
-// accumulator chaining), which is not the fp32 accumulation the fp8 scheme
-// calls for; the bf16 MFMA on the same values is accurate to fp32 rounding.  The weight fragment is the MFMA's A operand
-// and the token fragment its B operand, so each lane ends up holding four
-// consecutive output columns of one token row (8-byte bf16 stores).  K advances
-// 128 bytes per step through two LDS buffers (global loads for step k+1 are in
-// flight while step k computes; one barrier per step).  LDS rows are XOR
-// swizzled in 16-byte units so the MFMA operand reads are bank-conflict free.
-// Rows past M or past the weight's rows are loaded as zeros, which add exact
-// zeros to the accumulators.
+// Design.  Both operands are K-contiguous ("NT"), so MFMA operands load with no
+// transpose.  A workgroup of WGM x WGN waves owns a BM (tokens) x BN (weight
+// rows) tile; each wave accumulates a (BM/WGM) x (BN/WGN) sub-tile from 16x16
+// MFMA blocks: v_mfma_i32_16x16x64_i8 for int8; E4M3FN operands are widened
+// exactly to bf16 in registers and go through v_mfma_f32_16x16x32_bf16, because
+// the gfx950 fp8 MFMAs sum groups of products at roughly 14-bit precision
+// (measured: error ~2e-4 of the output rms at K = 4096 whatever the instruction
+// width or accumulator chaining) -- not the fp32 accumulation the fp8 scheme
+// calls for -- while the bf16 MFMA on the same values is accurate to fp32
+// rounding.  The weight fragment is the MFMA's A operand and the token fragment
+// its B operand, so a lane ends up holding four consecutive output columns of
+// one token row.
+//
+// Per-wave LDS traffic is (rows_m + rows_n) x K bytes for 2 rows_m rows_n K
+// ops, so the large 128 x 128 wave tiles of the 256 x 256 configuration need
+// half the LDS bandwidth per MFMA of 64 x 64 tiles.  K advances 64 bytes per
+// stage through a ring of kStages LDS buffers filled by direct-to-LDS loads
+// (global_load_lds_dwordx4: no staging registers, no LDS write instructions),
+// issued kStages - 1 stages ahead of use; one barrier per stage.  LDS rows are XOR-swizzled in 16-byte
+// units so the MFMA operand reads are bank-conflict free.  Rows past M or past
+// the weight's rows re-read the last valid row; they only reach outputs that
+// are never stored.
+//
+// Tile order: the hardware deals workgroups round-robin to the 8 XCDs (each
+// with its own L2), so block ids are remapped to give every XCD a contiguous
+// range of tiles, walked in groups of kGroupM token tiles so that concurrently
+// running tiles on one XCD share their token and weight panels in its L2.
 #include <type_traits>
 
 #include "internal.h"
@@ -35,24 +46,44 @@ namespace w8a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v8i __attribute__((ext_vector_type(8)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // staging (HIP's uint4 is a union
+                                                              // struct that defeats SROA)
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
 typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
-constexpr int BM = kGemmBM, BN = kGemmBN, BK = kGemmBK;
-constexpr int kThreads = 256;
-constexpr int kChunksPerRow = BK / 16;                              // 8 x 16 bytes
-constexpr int kLoadsPerThread = BM * kChunksPerRow / kThreads;     // 4
-constexpr int kTileBytes = BM * BK;                                // 16 KiB
+constexpr int kXcds = 8;
+constexpr int kGroupM = 4;
 
-// 16-byte chunk c of LDS row r is stored at chunk position c ^ f(r).
-__device__ __forceinline__ int swz(int r, int c) { return (r * kChunksPerRow + (c ^ (r & 7))) * 16; }
+// 16-byte chunk c of LDS row r (CH chunks per row) is stored at chunk position
+// c ^ swz_key<CH>(r).  An MFMA operand read has lanes fetch the same chunk of
+// consecutive rows; the key spreads every aligned group of 8 rows over 8
+// distinct 16-byte slots modulo 128 bytes and every aligned group of 16 rows
+// over 16 distinct slots modulo 256 bytes (verified exhaustively offline).
+template <int CH>
+__device__ __forceinline__ int swz_key(int r) {
+  if constexpr (CH == 4) return ((r >> 1) ^ (r >> 3)) & 3;
+  else return (r ^ (r >> 3)) & 7;
+}
+template <int CH>
+__device__ __forceinline__ int swz(int r, int c) { return (r * CH + (c ^ swz_key<CH>(r))) * 16; }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
 
 // Eight E4M3FN codes -> eight bf16 values (exact: every E4M3FN value, subnormals
 // included, is a bf16 value).
-__device__ __forceinline__ v8bf e4m3x8_to_bf16(uint2 v) {
+__device__ __forceinline__ v8bf e4m3x8_to_bf16(u32x2 v) {
   const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false);
   const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true);
   const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false);
@@ -68,227 +99,335 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
-template <Epi EPI>
-__device__ __forceinline__ int64_t weight_row(int r, int64_t nb, int64_t N) {
-  // LDS weight-tile row r -> global weight row (or -1 if out of range)
-  if constexpr (EPI == Epi::kSwiglu) {
-    const int64_t col = nb + (r & 63);                 // output column
-    if (col >= N) return -1;
-    return r < 64 ? col : N + col;                     // gate rows, then up rows
-  } else {
-    const int64_t n = nb + r;
-    return n < N ? n : -1;
-  }
+__device__ __forceinline__ void bf16x4(uint2 b, float* f) {
+  f[0] = __uint_as_float(b.x << 16);
+  f[1] = __uint_as_float(b.x & 0xffff0000u);
+  f[2] = __uint_as_float(b.y << 16);
+  f[3] = __uint_as_float(b.y & 0xffff0000u);
 }
 
-template <Epi EPI, bool FP8>
-__global__ void __launch_bounds__(kThreads)
+// Block id -> (tile_m, tile_n): contiguous tile ranges per XCD, grouped along M.
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
+                                              int& tm, int& tn) {
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  const int xcd = bid % kXcds, idx = bid / kXcds;
+  const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  const int per_group = kGroupM * tiles_n;
+  const int group = t / per_group, first_m = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - first_m);
+  const int in = t % per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+// 16 bytes from global memory straight into LDS.  The LDS address must be
+// wave-uniform (it goes to M0); lane i's bytes land at lds + 16 * i.  (The
+// builtin exists only for the device; the host pass just needs the kernel stub.)
+__device__ __forceinline__ void lds_dma16(const uint8_t* g, uint8_t* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+#endif
+}
+
+// Wait until at most n of this thread's vector-memory loads are outstanding.
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 s_waitcnt: vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[5:4] << 14
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8>
+__global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
           const uint8_t* __restrict__ b, const float* __restrict__ s_ch,
           const uint16_t* __restrict__ bias, void* __restrict__ out,
-          int64_t M, int64_t N, int64_t K, int tiles_m) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kTileBytes];  // [buf][a|b]
+          int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n) {
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int CH = BK / 16;                       // 16-byte chunks per LDS row
+  constexpr int NSUB = BK / 32;                     // 32-deep k substeps per stage
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;     // wave tile: tokens x weight rows
+  constexpr int TM = WTM / 32, TN = WTN / 32;       // 32x32 MFMA blocks per wave
+  constexpr int A_LOADS = BM * CH / NT, B_LOADS = BN * CH / NT;
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
+  constexpr int LOADS = A_LOADS + B_LOADS;          // per thread per stage
+  static_assert(NSUB % 2 == 0 && NST >= 2, "even substeps per stage, two or more stages");
+  static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "wave tiles of 32x32 blocks");
+  static_assert(A_LOADS * NT == BM * CH && B_LOADS * NT == BN * CH, "tile / threads");
+  static_assert(EPI != Epi::kSwiglu || TN % 2 == 0, "SwiGLU needs gate/up block pairs");
+  static_assert(NST * LOADS < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
-  const int tile_m = blockIdx.x % tiles_m;
-  const int tile_n = blockIdx.x / tiles_m;
+  const int wm = wave % WGM, wn = wave / WGM;
+  int tile_m, tile_n;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tile_m, tile_n);
   const int64_t mb = (int64_t)tile_m * BM;
-  // weight-row tile base: kSwiglu tiles cover 64 output columns (128 packed rows)
+  // SwiGLU tiles cover BN/2 output columns: LDS weight rows [0, BN/2) are gate
+  // rows, [BN/2, BN) the matching up rows.
   const int64_t nb = (EPI == Epi::kSwiglu) ? (int64_t)tile_n * (BN / 2) : (int64_t)tile_n * BN;
 
-  // Per-thread global source rows for the staged loads.
-  const uint8_t* a_src[kLoadsPerThread];
-  const uint8_t* b_src[kLoadsPerThread];
-  int lds_off[kLoadsPerThread];
+  // Direct-to-LDS loads: each wave instruction fills 64 consecutive 16-byte LDS
+  // slots; slot p of a stage holds chunk (p % CH) ^ swizzle of tile row p / CH,
+  // so each lane fetches the global chunk that belongs in its slot.  Offsets
+  // are 32-bit and relative to the tile's panel; rows past M (or past the
+  // weight's rows) re-read the last valid row -- they only reach outputs never
+  // stored.
+  const uint8_t* a_panel = a + mb * K;
+  const uint8_t* b_panel = b + nb * K;
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerThread; ++i) {
-    const int id = tid + i * kThreads;
-    const int r = id / kChunksPerRow, c = id % kChunksPerRow;
-    const int64_t am = mb + r;
-    a_src[i] = am < M ? a + am * K + c * 16 : nullptr;
-    const int64_t bn = weight_row<EPI>(r, nb, N);
-    b_src[i] = bn >= 0 ? b + bn * K + c * 16 : nullptr;
-    lds_off[i] = swz(r, c);
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
+    a_off[i] = (uint32_t)(min<int64_t>(r, M - 1 - mb) * K + c * 16);
   }
-
-  uint4 ra[kLoadsPerThread], rb[kLoadsPerThread];
-  auto gload = [&](int64_t k0) {
 #pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      ra[i] = a_src[i] ? *reinterpret_cast<const uint4*>(a_src[i] + k0) : make_uint4(0, 0, 0, 0);
-      rb[i] = b_src[i] ? *reinterpret_cast<const uint4*>(b_src[i] + k0) : make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
+    int64_t rel;  // weight row relative to nb
+    if constexpr (EPI == Epi::kSwiglu) {
+      const int64_t col = min<int64_t>(r % (BN / 2), N - 1 - nb);
+      rel = r < BN / 2 ? col : N + col;
+    } else {
+      rel = min<int64_t>(r, N - 1 - nb);
     }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < kLoadsPerThread; ++i) {
-      *reinterpret_cast<uint4*>(&lds[buf][0][lds_off[i]]) = ra[i];
-      *reinterpret_cast<uint4*>(&lds[buf][1][lds_off[i]]) = rb[i];
-    }
-  };
-
-  // Accumulators: [n sub-tile][m sub-tile], 16x16 each.
-  using Acc = typename std::conditional<FP8, v4f, v4i>::type;
-  Acc acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = Acc{0, 0, 0, 0};
-
-  // LDS rows this lane reads as MFMA operands.
-  const int frag_row = lane & 15, frag_grp = lane >> 4;
-  int b_rows[4], a_rows[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    a_rows[t] = wm * 64 + t * 16 + frag_row;
-    if constexpr (EPI == Epi::kSwiglu)
-      b_rows[t] = (t < 2 ? 0 : 64) + wn * 32 + (t & 1) * 16 + frag_row;
-    else
-      b_rows[t] = wn * 64 + t * 16 + frag_row;
+    b_off[i] = (uint32_t)(rel * K + c * 16);
   }
-
+  // Stages past the last one re-load the last stage into a buffer nobody reads
+  // again, so every stage issues the same number of loads (constant vmcnt
+  // accounting, no branches in the loop body).
   const int64_t ksteps = K / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
+  auto issue = [&](int64_t step) __attribute__((always_inline)) {
+    // 32-bit per-stage offsets off a uniform panel base: the loads use the
+    // scalar-base addressing form and keep one VGPR per load live, not two
+    const uint32_t k0 = (uint32_t)(min<int64_t>(step, ksteps - 1) * BK);
+    uint8_t* st = lds + (int)(step % NST) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) lds_dma16(a_panel + (a_off[i] + k0), st + (i * NT + wave * 64) * 16);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i)
+      lds_dma16(b_panel + (b_off[i] + k0), st + A_BYTES + (i * NT + wave * 64) * 16);
+  };
 
-  for (int64_t ks = 0; ks < ksteps; ++ks) {
-    const int buf = (int)(ks & 1);
-    if (ks + 1 < ksteps) gload((ks + 1) * BK);
-    const uint8_t* la = lds[buf][0];
-    const uint8_t* lb = lds[buf][1];
+  using Acc = typename std::conditional<FP8, v16f, v16i>::type;
+  Acc acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int j = 0; j < TM; ++j) acc[i][j] = Acc{};
+
+  // LDS rows this lane reads as MFMA operands: lane l supplies row l % 32 of a
+  // 32-row block; lane half h = l / 32 supplies k bytes [32j + 16h, +16) of
+  // substep j (for int8 one 32-deep MFMA; for E4M3FN two 16-deep bf16 MFMAs on
+  // bytes [0, 8) and [8, 16) of those 16 -- the same k pairing for both
+  // operands, which is all the dot product needs).
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+  int a_rows[TM], b_rows[TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) a_rows[t] = wm * WTM + t * 32 + frag_row;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    if constexpr (EPI == Epi::kSwiglu)
+      b_rows[t] = (t < TN / 2 ? 0 : BN / 2) + wn * (WTN / 2) + (t % (TN / 2)) * 32 + frag_row;
+    else
+      b_rows[t] = wn * WTN + t * 32 + frag_row;
+  }
+
+  // Two fragment register sets, alternating by substep: the next substep's
+  // fragments are read from LDS while the current one's MFMAs run.  (Set
+  // indices are compile-time constants so the arrays stay in registers.)
+  v4i fa[2][TM], fb[2][TN];
+  auto read_frags = [&](auto set_c, int64_t step, int sub) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    const uint8_t* la = lds + (int)(step % NST) * STAGE;
+    const uint8_t* lb = la + A_BYTES;
+    const int c = 2 * sub + frag_half;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) fa[set][t] = *reinterpret_cast<const v4i*>(la + swz<CH>(a_rows[t], c));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) fb[set][t] = *reinterpret_cast<const v4i*>(lb + swz<CH>(b_rows[t], c));
+  };
+  auto mfmas = [&](auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
     if constexpr (FP8) {
-      // E4M3FN codes are widened exactly to bf16 in registers and multiplied on
-      // the bf16 MFMA, which accumulates in fp32.  Per 32-k sub-block i, lane
-      // group g holds k bytes [32g + 8i, +8) of its row.
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v8bf fa[4], fb[4];
+      for (int j = 0; j < 2; ++j) {
+        v8bf ca[TM];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const int cb = 2 * frag_grp + (i >> 1), byte = (i & 1) * 8;
-          fa[t] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(la + swz(a_rows[t], cb) + byte));
-          fb[t] = e4m3x8_to_bf16(*reinterpret_cast<const uint2*>(lb + swz(b_rows[t], cb) + byte));
+        for (int t = 0; t < TM; ++t)
+          ca[t] = e4m3x8_to_bf16(u32x2{(unsigned)fa[set][t][2 * j], (unsigned)fa[set][t][2 * j + 1]});
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const v8bf cb = e4m3x8_to_bf16(u32x2{(unsigned)fb[set][tn][2 * j], (unsigned)fb[set][tn][2 * j + 1]});
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, ca[tm], acc[tn][tm], 0, 0, 0);
         }
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-          for (int tm = 0; tm < 4; ++tm)
-            acc[tn][tm] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[tn], fa[tm], acc[tn][tm], 0, 0, 0);
       }
     } else {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        // lane group g holds k bytes [64kk + 16g, +16)
-        v4i fa[4], fb[4];
+      for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint4 av = *reinterpret_cast<const uint4*>(la + swz(a_rows[t], 4 * kk + frag_grp));
-          const uint4 bv = *reinterpret_cast<const uint4*>(lb + swz(b_rows[t], 4 * kk + frag_grp));
-          fa[t] = v4i{(int)av.x, (int)av.y, (int)av.z, (int)av.w};
-          fb[t] = v4i{(int)bv.x, (int)bv.y, (int)bv.z, (int)bv.w};
-        }
-#pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
-#pragma unroll
-          for (int tm = 0; tm < 4; ++tm)
-            acc[tn][tm] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fb[tn], fa[tm], acc[tn][tm], 0, 0, 0);
-      }
+        for (int tm = 0; tm < TM; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][tn], fa[set][tm], acc[tn][tm], 0, 0, 0);
     }
-    if (ks + 1 < ksteps) lstore(buf ^ 1);
-    __syncthreads();
-  }
+  };
 
-  // ---- epilogue: lane holds rows n = 4*(lane/16) + v (v = 0..3), column m = lane % 16
-  const int n_in = 4 * frag_grp;
+  // Stage s lives in LDS buffer s % NST.  Stages 0 .. NST-1 are issued up front.
+  // In stage k, after substep NSUB-2 -- by then every read of stage k has been
+  // issued -- the wave waits until stage k + 1 has landed (its own loads:
+  // vmcnt; everyone's: the barrier), then refills buffer k % NST with stage
+  // k + NST while the last substep runs.  With one wave per SIMD any non-MFMA
+  // instruction between MFMAs idles the matrix core, so LDS reads and loads are
+  // interleaved one per MFMA (sched_group_barrier).
+  constexpr int NMFMA = TM * TN * (FP8 ? 2 : 1);   // MFMAs per substep
+  constexpr int NREAD = TM + TN;                    // ds_read_b128 per substep
+  constexpr int RD_PER = (NREAD + NMFMA - 1) / NMFMA;            // LDS reads per MFMA slot
+  constexpr int MEM_PER = (NREAD + LOADS + NMFMA - 1) / NMFMA;   // reads + loads per MFMA slot
 #pragma unroll
-  for (int tm = 0; tm < 4; ++tm) {
-    const int64_t m = mb + wm * 64 + tm * 16 + frag_row;
+  for (int s = 0; s < NST; ++s) issue(s);
+  wait_vmcnt<(NST - 1) * LOADS>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  read_frags(std::integral_constant<int, 0>{}, 0, 0);
+
+  for (int64_t ks = 0; ks < ksteps; ++ks) {
+    static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
+      constexpr int j = decltype(j_c)::value;
+      constexpr int cur = j & 1;
+      if constexpr (j < NSUB - 1) {
+        // prefetch substep j + 1 of this stage while multiplying substep j
+        read_frags(std::integral_constant<int, cur ^ 1>{}, ks, j + 1);
+        mfmas(std::integral_constant<int, cur>{});
+#pragma unroll
+        for (int i = 0; i < NMFMA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, j);       // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, RD_PER, j);  // LDS reads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (j == NSUB - 2) {
+          // every read of stage ks is issued; stage ks + 1 landed (stages
+          // ks + 2 .. ks + NST - 1 may still be in flight); then everyone's
+          wait_vmcnt<(NST - 2) * LOADS>();
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+          __builtin_amdgcn_s_barrier();
+          asm volatile("" ::: "memory");
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        // last substep: refill buffer ks % NST, prefetch substep 0 of the next stage
+        issue(ks + NST);
+        read_frags(std::integral_constant<int, cur ^ 1>{}, ks + 1, 0);
+        mfmas(std::integral_constant<int, cur>{});
+#pragma unroll
+        for (int i = 0; i < NMFMA; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, j);        // one MFMA
+          __builtin_amdgcn_sched_group_barrier(0x120, MEM_PER, j);  // LDS reads, loads
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    });
+  }
+  // the tail re-loads must land before the workgroup's LDS can be reused
+  wait_vmcnt<0>();
+
+  // ---- epilogue.  32x32 block layout: lane l holds token column l % 32 and, in
+  // registers 4q .. 4q+3, weight rows 8q + 4 * (l / 32) + 0..3 of the block.
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int64_t m = mb + wm * WTM + tm * 32 + frag_row;
     if (m >= M) continue;
     if constexpr (EPI == Epi::kRawI32) {
 #pragma unroll
-      for (int tn = 0; tn < 4; ++tn) {
-        const int64_t n0 = nb + wn * 64 + tn * 16 + n_in;
-        if (n0 >= N) continue;
-        const v4i v = reinterpret_cast<const v4i&>(acc[tn][tm]);
-        *reinterpret_cast<int4*>(static_cast<int32_t*>(out) + m * N + n0) = make_int4(v.x, v.y, v.z, v.w);
-      }
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t n0 = nb + wn * WTN + tn * 32 + 8 * q + 4 * frag_half;
+          if (n0 >= N) continue;
+          const v16i& v = reinterpret_cast<const v16i&>(acc[tn][tm]);
+          *reinterpret_cast<int4*>(static_cast<int32_t*>(out) + m * N + n0) =
+              make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        }
     } else {
       const float st = s_tok[m];
       uint16_t* yrow = static_cast<uint16_t*>(out) + m * N;
       if constexpr (EPI == Epi::kDequant) {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-          const int64_t n0 = nb + wn * 64 + tn * 16 + n_in;
-          if (n0 >= N) continue;
-          const float4 sc = *reinterpret_cast<const float4*>(s_ch + n0);
-          float bv[4] = {0.f, 0.f, 0.f, 0.f};
-          if (bias) {
-            const uint2 bb = *reinterpret_cast<const uint2*>(bias + n0);
-            bv[0] = __uint_as_float(bb.x << 16);
-            bv[1] = __uint_as_float(bb.x & 0xffff0000u);
-            bv[2] = __uint_as_float(bb.y << 16);
-            bv[3] = __uint_as_float(bb.y & 0xffff0000u);
-          }
-          const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-          uint16_t o[4];
+        for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float av = (float)acc[tn][tm][v];
-            o[v] = f32_to_bf16_rne(__builtin_fmaf(av, st * scv[v], bv[v]));
-          }
-          *reinterpret_cast<uint2*>(yrow + n0) =
-              make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-        }
-      } else {  // kSwiglu: sub-tiles 0,1 are gate, 2,3 the matching up rows
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n0 = nb + wn * WTN + tn * 32 + 8 * q + 4 * frag_half;
+            if (n0 >= N) continue;
+            const float4 sc = *reinterpret_cast<const float4*>(s_ch + n0);
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bv);
+            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+            uint16_t o[4];
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) {
-          const int64_t n0 = nb + wn * 32 + tn * 16 + n_in;  // output column
-          if (n0 >= N) continue;
-          const float4 sg = *reinterpret_cast<const float4*>(s_ch + n0);
-          const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n0);
-          float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-          if (bias) {
-            const uint2 b0 = *reinterpret_cast<const uint2*>(bias + n0);
-            const uint2 b1 = *reinterpret_cast<const uint2*>(bias + N + n0);
-            bg[0] = __uint_as_float(b0.x << 16); bg[1] = __uint_as_float(b0.x & 0xffff0000u);
-            bg[2] = __uint_as_float(b0.y << 16); bg[3] = __uint_as_float(b0.y & 0xffff0000u);
-            bu[0] = __uint_as_float(b1.x << 16); bu[1] = __uint_as_float(b1.x & 0xffff0000u);
-            bu[2] = __uint_as_float(b1.y << 16); bu[3] = __uint_as_float(b1.y & 0xffff0000u);
+            for (int v = 0; v < 4; ++v)
+              o[v] = f32_to_bf16_rne(__builtin_fmaf((float)acc[tn][tm][4 * q + v], st * scv[v], bv[v]));
+            *reinterpret_cast<uint2*>(yrow + n0) =
+                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
           }
-          const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
-          uint16_t o[4];
+      } else {  // kSwiglu: blocks [0, TN/2) are gate, [TN/2, TN) the matching up rows
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float g = __builtin_fmaf((float)acc[tn][tm][v], st * sgv[v], bg[v]);
-            const float u = __builtin_fmaf((float)acc[tn + 2][tm][v], st * suv[v], bu[v]);
-            const float silu = g / (1.0f + __expf(-g));
-            o[v] = f32_to_bf16_rne(silu * u);
+        for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t n0 = nb + wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half;  // output column
+            if (n0 >= N) continue;
+            const float4 sg = *reinterpret_cast<const float4*>(s_ch + n0);
+            const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n0);
+            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+              bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bg);
+              bf16x4(*reinterpret_cast<const uint2*>(bias + N + n0), bu);
+            }
+            const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+            uint16_t o[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
+              const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
+              o[v] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
+            }
+            *reinterpret_cast<uint2*>(yrow + n0) =
+                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
           }
-          *reinterpret_cast<uint2*>(yrow + n0) =
-              make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-        }
       }
     }
   }
 }
 
-template <Epi EPI, bool FP8>
-hipError_t launch_t(const void* a, const float* s_tok, const void* b, const float* s_ch,
-                    const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
-                    hipStream_t stream) {
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8>
+hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const float* s_ch,
+                      const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
+                      hipStream_t stream) {
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t cols_per_tile = (EPI == Epi::kSwiglu) ? BN / 2 : BN;
   const int64_t tiles_n = (N + cols_per_tile - 1) / cols_per_tile;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_tile<EPI, FP8>), dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                     static_cast<const uint8_t*>(a), s_tok, static_cast<const uint8_t*>(b), s_ch, bias,
-                     out, M, N, K, (int)tiles_m);
+  hipLaunchKernelGGL((gemm_tile<BM, BN, WGM, WGN, BK, NST, EPI, FP8>), dim3((unsigned)blocks),
+                     dim3(64 * WGM * WGN), 0, stream, static_cast<const uint8_t*>(a), s_tok,
+                     static_cast<const uint8_t*>(b), s_ch, bias, out, M, N, K, (int)tiles_m,
+                     (int)tiles_n);
   return hipGetLastError();
+}
+
+// Tile choice: 256 x 256 (8 waves of 128 x 64) when it still fills the chip,
+// 128 x 128 (4 waves of 64 x 64) for small problems.
+template <Epi EPI, bool FP8>
+hipError_t launch_t(const void* a, const float* s_tok, const void* b, const float* s_ch,
+                    const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
+                    hipStream_t stream) {
+  const int64_t nw = (EPI == Epi::kSwiglu) ? 2 * N : N;  // weight rows
+  const int64_t big_tiles = ((M + 255) / 256) * ((nw + 255) / 256);
+  if (big_tiles >= 256)
+    return launch_cfg<256, 256, 2, 2, 64, 4, EPI, FP8>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  return launch_cfg<128, 128, 2, 2, 64, 4, EPI, FP8>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
 }
 
 }  // namespace

@@ -7,11 +7,6 @@
 
 namespace w8a8 {
 
-// Output tile of the GEMM kernels: BM token rows x BN weight rows, K step BK bytes.
-constexpr int kGemmBM = 128;
-constexpr int kGemmBN = 128;
-constexpr int kGemmBK = 128;
-
 // Epilogues of the GEMM kernel.
 enum class Epi : int { kRawI32 = 0, kDequant = 1, kSwiglu = 2 };
 
