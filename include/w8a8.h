@@ -45,7 +45,7 @@
  *     asynchronous HIP call.
  *   - Inputs must be finite; results for non-finite inputs are unspecified.
  *   - Shape limits: M >= 0; 1 <= K <= W8A8_MAX_K and K % 128 == 0 for the GEMM
- *     entry points (K % 16 == 0 for the quantizers alone; K % 128 == 0 whenever
+ *     entry points (K % 32 == 0 for the quantizers alone; K % 128 == 0 whenever
  *     rot_block == 128); N >= 1 and N % 8 == 0; rot_block is 0 or 128.
  *     W8A8_MAX_K keeps every int8 accumulator (|acc| <= 127*127*K) inside int32.
  *   - Entry points are reentrant; the only global state is a per-device cache

@@ -84,7 +84,8 @@ def test_quantize_argument_checks(lib):
     assert q(A, 4, 128, 0, A, None, None) == NULLP
     assert q(A, -1, 128, 0, A, A, None) == SHAPE
     assert q(A, 4, 0, 0, A, A, None) == SHAPE
-    assert q(A, 4, 24, 0, A, A, None) == SHAPE               # K % 16
+    assert q(A, 4, 24, 0, A, A, None) == SHAPE               # K % 32
+    assert q(A, 4, 48, 0, A, A, None) == SHAPE
     assert q(A, 4, 131072 + 16, 0, A, A, None) == SHAPE      # K > max
     assert q(A, 4, 64, 128, A, A, None) == SHAPE             # rotation needs K % 128
     assert q(A, 4, 128, 64, A, A, None) == BADARG            # rot_block not 0/128

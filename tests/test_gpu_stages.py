@@ -34,7 +34,8 @@ def _x_case(M, K, rot, seed, zero_rows=()):
 
 
 QUANT_CASES = [
-    (298, 1024, 0), (1, 16, 0), (7, 48, 0), (5, 5120, 0), (3, 17408, 0), (2, 131072, 0),
+    (298, 1024, 0), (1, 32, 0), (7, 96, 0), (5, 5120, 0), (3, 17408, 0), (2, 131072, 0),
+    (600, 4096, 0), (1502, 4096, 128), (129, 5120, 128),
     (300, 1024, 128), (64, 4096, 128), (9, 17408, 128), (2, 131072, 128), (5, 5120, 128),
 ]
 
@@ -50,7 +51,7 @@ def test_quantize_int8(lib, orc, M, K, rot):
     assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "scales differ"
 
 
-@pytest.mark.parametrize("M,K,rot", [(298, 1024, 0), (3, 48, 0), (4, 17408, 0), (33, 4096, 128),
+@pytest.mark.parametrize("M,K,rot", [(298, 1024, 0), (3, 96, 0), (4, 17408, 0), (33, 4096, 128),
                                      (3, 17408, 128), (2, 131072, 0)])
 def test_quantize_fp8(lib, orc, M, K, rot):
     say(f"quantize fp8 M={M} K={K} rot={rot}")

@@ -52,7 +52,7 @@ w8a8_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 // OK with any pointers once the shapes are legal.
 w8a8_status quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, bool fp8, void* q,
                      float* s, hipStream_t stream) {
-  if (M < 0 || K < 16 || K > W8A8_MAX_K || K % 16 != 0 || M > (int64_t)1 << 31) return W8A8_ERR_BAD_SHAPE;
+  if (M < 0 || K < 32 || K > W8A8_MAX_K || K % 32 != 0 || M > (int64_t)1 << 31) return W8A8_ERR_BAD_SHAPE;
   if (rot_block != 0 && rot_block != 128) return W8A8_ERR_BAD_ARGUMENT;
   if (rot_block == 128 && K % 128 != 0) return W8A8_ERR_BAD_SHAPE;
   if (M == 0) return W8A8_OK;

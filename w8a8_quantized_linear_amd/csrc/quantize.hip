@@ -11,23 +11,29 @@
 // clamp(y/s, +-448)); a zero row gives s = 0 and zero codes.
 //
 // Design (HBM bound: 2 bytes read + 1 byte written per element):
-//   * T threads own one row; each lane holds chunks of 16 consecutive bf16
-//     (32 bytes, two 16-byte loads), all loads of a lane issued before any math.
+//   * T threads own one row; each lane holds chunks of 32 elements (four
+//     16-byte loads), all loads of a lane issued before any math: with rotation
+//     32 consecutive elements, without it pieces laid out so that each wave
+//     load instruction reads one contiguous kilobyte.
 //   * Rotation is exact: the block sums of 128 bf16 values are formed in fp64
 //     (exact for 8-bit significands unless the block's exponent spread exceeds
-//     ~38 bits) with 4 butterfly stages inside a lane and 3 across the 8 lanes
-//     that share a block, then multiplied by fl64(2^-3.5) and rounded once to
-//     fp32.  The quantized codes are therefore those of the exactly rotated row.
-//   * amax by wave butterfly (shfl_xor) plus an LDS step across the row's waves.
-//   * Codes use an IEEE fp32 division by s (correctly rounded), v_rndne_f32, and
-//     for fp8 the hardware RNE converter after clamping to +-448.
-//   * 16-byte coalesced stores of the codes.
+//     ~38 bits) -- 5 butterfly stages inside a lane, the last 2 across the 4
+//     lanes of a DPP quad (quad_perm moves, no LDS) -- then multiplied by
+//     fl64(2^-3.5) and rounded once to fp32.  The codes are therefore those of
+//     the exactly rotated row.
+//   * amax by wave butterfly plus an LDS step across the row's waves.
+//   * int8 codes: t = y * fl32(1/s), k = rint(t).  t is within 2 ulps of the
+//     IEEE quotient y / s, so k is the code of fl32(y / s) unless t lies within
+//     a few ulps of a half-integer; those rare elements are redone with the
+//     IEEE division.  E4M3FN codes use the IEEE division and the hardware RNE
+//     converter after clamping to +-448.
+//   * 8-byte stores of the codes (contiguous across the wave without rotation).
 #include "internal.h"
 
 namespace w8a8 {
 namespace {
 
-constexpr int kEPL = 16;  // bf16 elements per lane per chunk
+constexpr int kEPL = 32;  // bf16 elements per lane per chunk
 
 // fl64(2^-3.5) = fl64(sqrt(2)/2) / 8
 constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;
@@ -41,55 +47,86 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// fp64 value of the lane whose quad position differs in the bits of MASK (1 or 2).
+template <int MASK>
+__device__ __forceinline__ double quad_xor(double v) {
+  // quad_perm selectors: lane i of each quad reads lane i ^ MASK
+  constexpr int ctrl = MASK == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] / [2,3,0,1]
+  const long long bits = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_mov_dpp((int)bits, ctrl, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_mov_dpp((int)(bits >> 32), ctrl, 0xF, 0xF, false);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
+}
+
 __device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
   uint32_t ia = (uint32_t)(int)a & 0xffu, ib = (uint32_t)(int)b & 0xffu;
   uint32_t ic = (uint32_t)(int)c & 0xffu, id = (uint32_t)(int)d & 0xffu;
   return ia | (ib << 8) | (ic << 16) | (id << 24);
 }
 
-// T threads per row (64, 256 or 1024), CMAX chunks of 16 elements per lane.
+// Code of fl32(y / s) rounded half to even, via the reciprocal r = fl32(1/s).
+__device__ __forceinline__ float int8_code(float y, float s, float r) {
+  const float t = y * r;
+  const float k = __builtin_rintf(t);
+  // |t - y/s| <= 2^-16 and |fl32(y/s) - y/s| <= 2^-18 for |y/s| < 128: only a t
+  // within 2^-15 of a half-integer can round differently from the IEEE
+  // quotient.  (Written so that a non-finite t, from a subnormal s, also takes
+  // the exact path.)
+  if (__builtin_expect(!(fabsf(fabsf(t - k) - 0.5f) >= 0x1p-14f), 0)) return __builtin_rintf(y / s);
+  return k;
+}
+
+// T threads per row (a multiple of 64), CMAX chunks of 32 elements per lane.
+template <int T>
+constexpr int rows_per_block() { return (T < 256 && 256 % T == 0) ? 256 / T : 1; }
+
 template <int T, int CMAX, bool ROT, bool FP8>
-__global__ void __launch_bounds__(T < 256 ? 256 : T)
+__global__ void __launch_bounds__(T * rows_per_block<T>())
 quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restrict__ q,
               float* __restrict__ s_out) {
-  constexpr int kRowsPerBlock = T < 256 ? 256 / T : 1;
+  constexpr int kRowsPerBlock = rows_per_block<T>();
+  constexpr int kWavesPerRow = T / 64;
   const int tid = threadIdx.x % T;
   const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + threadIdx.x / T;
   const int lane = threadIdx.x & 63;
-  const int nchunks = K / kEPL;
-  // Rows past M: the whole T-group leaves together (T is a multiple of 64 and a
-  // block holds several rows only when T == 64, where no block barrier is used).
-  if (row >= M) return;
-
-  const uint16_t* xr = x + row * (int64_t)K;
-  uint4 raw[CMAX][2];
+  // A row past M (only in the last block) is computed on row M - 1 and not
+  // stored, so that every wave reaches the block barrier below.
+  const bool live = row < M;
+  const uint16_t* xr = x + (live ? row : M - 1) * (int64_t)K;
+  typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  // A lane's chunk i is four pieces of 8 elements.  With rotation the pieces are
+  // consecutive (32 contiguous elements: a quarter of a 128-block per lane).
+  // Without rotation any placement works, so the wave's 64 lanes take
+  // consecutive 16-byte pieces of a 2048-element span: every load and store
+  // instruction then covers one contiguous kilobyte (half as many cache lines
+  // per instruction as 64-byte-strided lanes).
+  auto piece = [&](int i, int p) -> int {
+    if constexpr (ROT) return (i * T + tid) * kEPL + 8 * p;
+    else return (i * (T / 64) + tid / 64) * (64 * kEPL) + p * 512 + lane * 8;
+  };
+  u32x4 raw[CMAX][4];
 #pragma unroll
-  for (int i = 0; i < CMAX; ++i) {
-    const int c = i * T + tid;
-    if (c < nchunks) {
-      const uint4* p = reinterpret_cast<const uint4*>(xr + (int64_t)c * kEPL);
-      raw[i][0] = p[0];
-      raw[i][1] = p[1];
-    } else {
-      raw[i][0] = make_uint4(0, 0, 0, 0);
-      raw[i][1] = make_uint4(0, 0, 0, 0);
+  for (int i = 0; i < CMAX; ++i)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int e = piece(i, v);
+      raw[i][v] = e < K ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(xr + e)) : u32x4{0, 0, 0, 0};
     }
-  }
 
   float y[CMAX][kEPL];
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < CMAX; ++i) {
-    const uint32_t w[8] = {raw[i][0].x, raw[i][0].y, raw[i][0].z, raw[i][0].w,
-                           raw[i][1].x, raw[i][1].y, raw[i][1].z, raw[i][1].w};
     if constexpr (ROT) {
       double v[kEPL];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        v[2 * j] = (double)bf16lo(w[j]);
-        v[2 * j + 1] = (double)bf16hi(w[j]);
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t w = raw[i][j / 4][j % 4];
+        v[2 * j] = (double)bf16lo(w);
+        v[2 * j + 1] = (double)bf16hi(w);
       }
-      // element index bits 0..3 live in the lane
+      // element index bits 0..4 live in the lane
 #pragma unroll
       for (int h = 1; h < kEPL; h <<= 1) {
 #pragma unroll
@@ -101,82 +138,97 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
           }
         }
       }
-      // element index bits 4..6 are lane bits 0..2 (8 lanes per block of 128)
+      // element index bits 5, 6 are the lane's position in its quad
+      {
+        const double sgn = (lane & 1) ? -1.0 : 1.0;
 #pragma unroll
-      for (int h = 1; h < 8; h <<= 1) {
-        const double sgn = (lane & h) ? -1.0 : 1.0;
-#pragma unroll
-        for (int j = 0; j < kEPL; ++j) {
-          const double p = __shfl_xor(v[j], h, 64);
-          v[j] = __builtin_fma(sgn, v[j], p);  // lower lane: v + p; upper lane: p - v (exact)
-        }
+        for (int j = 0; j < kEPL; ++j) v[j] = __builtin_fma(sgn, v[j], quad_xor<1>(v[j]));
       }
+      {
+        const double sgn = (lane & 2) ? -1.0 : 1.0;
+#pragma unroll
+        for (int j = 0; j < kEPL; ++j) v[j] = __builtin_fma(sgn, v[j], quad_xor<2>(v[j]));
+      }
+      // (lower lane: v + p; upper lane: p - v; both exact)
 #pragma unroll
       for (int j = 0; j < kEPL; ++j) y[i][j] = (float)(v[j] * kInvSqrt128);
     } else {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        y[i][2 * j] = bf16lo(w[j]);
-        y[i][2 * j + 1] = bf16hi(w[j]);
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t w = raw[i][j / 4][j % 4];
+        y[i][2 * j] = bf16lo(w);
+        y[i][2 * j + 1] = bf16hi(w);
       }
     }
-    const bool valid = (i * T + tid) < nchunks;
+    // (pieces past K hold zeros, which leave the amax unchanged)
 #pragma unroll
-    for (int j = 0; j < kEPL; ++j) amax = valid ? fmaxf(amax, fabsf(y[i][j])) : amax;
+    for (int j = 0; j < kEPL; ++j) amax = fmaxf(amax, fabsf(y[i][j]));
   }
 
   amax = wave_max(amax);
-  if constexpr (T > 64) {
-    __shared__ float red[T / 64];
-    if (lane == 0) red[threadIdx.x / 64] = amax;
+  if constexpr (kWavesPerRow > 1) {
+    __shared__ float red[kWavesPerRow * kRowsPerBlock];
+    const int wave_in_block = threadIdx.x / 64;
+    if (lane == 0) red[wave_in_block] = amax;
     __syncthreads();
+    const int first = (threadIdx.x / T) * kWavesPerRow;
 #pragma unroll
-    for (int wv = 0; wv < T / 64; ++wv) amax = fmaxf(amax, red[wv]);
+    for (int wv = 0; wv < kWavesPerRow; ++wv) amax = fmaxf(amax, red[first + wv]);
   }
 
   constexpr float kQmax = FP8 ? 448.0f : 127.0f;
   const float s = amax / kQmax;  // IEEE division
+  if (!live) return;
   if (tid == 0) s_out[row] = s;
   const bool zero_row = !(amax > 0.0f);
+  const float r = zero_row ? 0.0f : 1.0f / s;
 
   uint8_t* qr = q + row * (int64_t)K;
 #pragma unroll
   for (int i = 0; i < CMAX; ++i) {
-    const int c = i * T + tid;
-    if (c >= nchunks) continue;
-    uint32_t out[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      float t[4];
+    for (int v = 0; v < 4; ++v) {
+      const int e0 = piece(i, v);
+      if (e0 >= K) continue;
+      uint32_t out[2];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = zero_row ? 0.0f : y[i][4 * g + e] / s;
-      if constexpr (FP8) {
+      for (int g = 0; g < 2; ++g) {
+        float t[4];
+        if constexpr (FP8) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(t[e], -448.0f), 448.0f);
-        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
-        wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], wd, true);
-        out[g] = (uint32_t)wd;
-      } else {
+          for (int e = 0; e < 4; ++e) {
+            t[e] = zero_row ? 0.0f : y[i][8 * v + 4 * g + e] / s;
+            t[e] = fminf(fmaxf(t[e], -448.0f), 448.0f);
+          }
+          int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
+          wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], wd, true);
+          out[g] = (uint32_t)wd;
+        } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = fminf(fmaxf(__builtin_rintf(t[e]), -127.0f), 127.0f);
-        out[g] = pack_i8x4(t[0], t[1], t[2], t[3]);
+          for (int e = 0; e < 4; ++e) {
+            const float k = zero_row ? 0.0f : int8_code(y[i][8 * v + 4 * g + e], s, r);
+            t[e] = fminf(fmaxf(k, -127.0f), 127.0f);
+          }
+          out[g] = pack_i8x4(t[0], t[1], t[2], t[3]);
+        }
       }
+      *reinterpret_cast<u32x2*>(qr + e0) = u32x2{out[0], out[1]};
     }
-    *reinterpret_cast<uint4*>(qr + (int64_t)c * kEPL) = make_uint4(out[0], out[1], out[2], out[3]);
   }
 }
 
 template <int T, bool ROT, bool FP8>
-hipError_t dispatch_cmax(int cmax, dim3 grid, const uint16_t* x, int64_t M, int K, uint8_t* q,
-                         float* s, hipStream_t stream) {
-  const dim3 block(T < 256 ? 256 : T);
+hipError_t dispatch_cmax(int cmax, const uint16_t* x, int64_t M, int K, uint8_t* q, float* s,
+                         hipStream_t stream) {
+  constexpr int kRowsPerBlock = rows_per_block<T>();
+  const dim3 block(T * kRowsPerBlock);
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
   switch (cmax) {
 #define W8A8_Q_CASE(C)                                                                     \
   case C:                                                                                  \
     hipLaunchKernelGGL((quantize_rows<T, C, ROT, FP8>), grid, block, 0, stream, x, M, K, q, s); \
     break;
     W8A8_Q_CASE(1) W8A8_Q_CASE(2) W8A8_Q_CASE(3) W8A8_Q_CASE(4)
-    W8A8_Q_CASE(5) W8A8_Q_CASE(6) W8A8_Q_CASE(7) W8A8_Q_CASE(8)
 #undef W8A8_Q_CASE
     default:
       return hipErrorInvalidValue;
@@ -184,21 +236,31 @@ hipError_t dispatch_cmax(int cmax, dim3 grid, const uint16_t* x, int64_t M, int 
   return hipGetLastError();
 }
 
+// Threads per row: the multiple of 64 (up to 256) whose chunk slots waste the
+// fewest lanes with at most 4 chunks per lane; rows longer than 4 x 256 chunks
+// (K > 32768) use 1024 threads.
 template <bool ROT, bool FP8>
 hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float* s,
                          hipStream_t stream) {
   const int nchunks = K / kEPL;
-  if (nchunks <= 64 * 8) {
-    const int cmax = (nchunks + 63) / 64;
-    const dim3 grid((unsigned)((M + 3) / 4));
-    return dispatch_cmax<64, ROT, FP8>(cmax, grid, x, M, K, q, s, stream);
+  if (nchunks > 4 * 256) {
+    const int cmax = (nchunks + 1023) / 1024;
+    if (cmax > 4) return hipErrorInvalidValue;
+    return dispatch_cmax<1024, ROT, FP8>(cmax, x, M, K, q, s, stream);
   }
-  if (nchunks <= 256 * 8) {
-    const int cmax = (nchunks + 255) / 256;
-    return dispatch_cmax<256, ROT, FP8>(cmax, dim3((unsigned)M), x, M, K, q, s, stream);
+  int best_t = 256, best_slots = 1 << 30;
+  for (int t = 64; t <= 256; t += 64) {
+    const int cmax = (nchunks + t - 1) / t;
+    if (cmax > 4) continue;
+    if (t * cmax < best_slots) { best_slots = t * cmax; best_t = t; }
   }
-  const int cmax = (nchunks + 1023) / 1024;
-  return dispatch_cmax<1024, ROT, FP8>(cmax, dim3((unsigned)M), x, M, K, q, s, stream);
+  const int cmax = (nchunks + best_t - 1) / best_t;
+  switch (best_t) {
+    case 64: return dispatch_cmax<64, ROT, FP8>(cmax, x, M, K, q, s, stream);
+    case 128: return dispatch_cmax<128, ROT, FP8>(cmax, x, M, K, q, s, stream);
+    case 192: return dispatch_cmax<192, ROT, FP8>(cmax, x, M, K, q, s, stream);
+    default: return dispatch_cmax<256, ROT, FP8>(cmax, x, M, K, q, s, stream);
+  }
 }
 
 }  // namespace
