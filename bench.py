@@ -34,6 +34,7 @@ PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP8_TFLOPS = 5000.0     # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # HBM3E 8 TB/s
 ROTATION_BYTES = 512 << 20
+CALIBRATION_BYTES = 256 << 20   # plain device copy run before the warmup (counter calibration)
 
 
 def parse():
@@ -43,6 +44,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script into "
+                         "profiles/traffic_<workload>.json and exit")
     return ap.parse_args()
 
 
@@ -63,6 +67,53 @@ def stored_traffic(workload: str):
     if rec.get("sources_digest") != kernel_sources_digest():
         return None
     return rec.get("gemm_bytes_per_launch")
+
+
+def _pmc_per_kernel(run_dir: str, counter: str):
+    """Mean counter value (KiB per dispatch) per kernel name from a rocprofv3 csv run."""
+    import csv
+    import glob
+    vals = {}
+    for f in glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True):
+        per_dispatch = {}
+        for r in csv.DictReader(open(f)):
+            if r["Counter_Name"] != counter:
+                continue
+            key = (r["Dispatch_Id"], r["Kernel_Name"])
+            per_dispatch[key] = per_dispatch.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name), v in per_dispatch.items():
+            vals.setdefault(name, []).append(v)
+    return vals
+
+
+def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> dict:
+    """HBM bytes per GEMM launch from FETCH_SIZE / WRITE_SIZE, each scaled by the factor
+    that makes the calibration copy read / write exactly CALIBRATION_BYTES."""
+    fetch = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    write = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+
+    def pick(d, pred):
+        ks = [k for k in d if pred(k)]
+        if not ks:
+            raise SystemExit(f"no kernel matching in {sorted(d)[:5]}")
+        return ks
+    # the calibration add reads and writes CALIBRATION_BYTES (the largest elementwise
+    # kernel in the run); the GEMM is gemm_tile
+    copy_k = max(pick(fetch, lambda k: "elementwise" in k.lower()), key=lambda k: max(fetch[k]))
+    gemm_k = pick(fetch, lambda k: "gemm_tile" in k)[0]
+    copy_w = max(pick(write, lambda k: "elementwise" in k.lower()), key=lambda k: max(write[k]))
+    f_copy, w_copy = max(fetch[copy_k]), max(write[copy_w])
+    f_factor = CALIBRATION_BYTES / (f_copy * 1024.0)
+    w_factor = CALIBRATION_BYTES / (w_copy * 1024.0)
+    f_gemm = sum(fetch[gemm_k]) / len(fetch[gemm_k])
+    w_gemm = sum(write[gemm_k]) / len(write[gemm_k])
+    rec = {"workload": workload, "sources_digest": kernel_sources_digest(),
+           "gemm_kernel": gemm_k.split("(")[0], "gemm_dispatches": len(fetch[gemm_k]),
+           "fetch_kib_per_launch": f_gemm, "write_kib_per_launch": w_gemm,
+           "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
+           "fetch_factor": f_factor, "write_factor": w_factor,
+           "gemm_bytes_per_launch": f_gemm * 1024.0 * f_factor + w_gemm * 1024.0 * w_factor}
+    return rec
 
 
 def cpu_baseline(wl, inp):
@@ -90,9 +141,15 @@ def cpu_baseline(wl, inp):
 
 def main():
     args = parse()
+    if args.pmc_summary:
+        rec = pmc_summary(args.workload, *args.pmc_summary)
+        out = ROOT / "profiles" / f"traffic_{args.workload}.json"
+        out.write_text(json.dumps(rec, indent=1) + "\n")
+        print(json.dumps(rec, indent=1))
+        return
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(the projection shards by token rows with no exchange; see the design notes)",
+              "(across GPUs the projection would shard by token rows, with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -103,6 +160,13 @@ def main():
     wl = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # untimed elementwise kernel of known size (reads and writes CALIBRATION_BYTES):
+    # the reference the HBM byte counters are scaled by
+    calib_src = torch.zeros(CALIBRATION_BYTES // 4, dtype=torch.float32, device=dev)
+    calib_dst = torch.empty_like(calib_src)
+    torch.add(calib_src, 1.0, out=calib_dst)
+    torch.cuda.synchronize()
+    del calib_src, calib_dst
     inp = W.make_inputs(wl)
     fp8 = wl.kind == "fp8"
     quant = lib.w8a8_quantize_act_fp8 if fp8 else lib.w8a8_quantize_act
