@@ -4,12 +4,15 @@
 
 One step is one pass of the whole hot path over one batch: the per-token
 quantizer (stage 1) followed by the int8 GEMM with its fused epilogue (stages 2
-and 3) -- the two kernels ``w8a8_linear`` / ``w8a8_gateup_swiglu`` /
-``w8a8_fp8_linear`` enqueue, launched here through their stage entry points so
-that each kernel is bracketed by HIP events on the launch stream.  Inputs
-(activations, quantized weights, scales, bias) are resident in HBM before the
-timed region; successive steps rotate through enough copies of them (>= 512 MiB
-in total) that no step finds its operands in the 256 MiB last-level cache.
+and 3) -- the two kernels ``w8a8_linear_packed`` / ``w8a8_gateup_swiglu_packed`` /
+``w8a8_fp8_linear_packed`` enqueue (activation codes written in the packed
+layout, weight packed once at load time), launched here through their stage
+entry points (``w8a8_quantize_act*_packed`` and the ``*_packed`` GEMMs) so that
+each kernel is bracketed by HIP events on the launch stream.  Inputs
+(activations, quantized and packed weights, scales, bias) are resident in HBM
+before the timed region; successive steps rotate through enough copies of them
+(>= 512 MiB in total) that no step finds its operands in the 256 MiB
+last-level cache.
 
 Prints one JSON line: metric = TOPS of the whole path (2*M*N_w*K ops per step
 over the step time), the roofline of the dominant kernel (the GEMM) with its
@@ -175,21 +178,25 @@ def main():
 
     # resident operands, several copies so that consecutive steps do not hit in cache
     x0 = inp.x.to(dev)
-    wq0, s_ch0 = quant(inp.w.to(dev), wl.rot_block)
+    wq_rows, s_ch0 = quant(inp.w.to(dev), wl.rot_block)
+    wq0 = lib.w8a8_pack_weight(wq_rows)       # load-time packing, outside the timed region
+    del wq_rows
     bias0 = None if inp.bias is None else inp.bias.to(dev)
     per_copy = M * K * 2 + Nw * K + M * K + M * n_out * 2 + 4 * (M + Nw)
     copies = max(2, -(-ROTATION_BYTES // per_copy))
     xs = [x0] + [x0.clone() for _ in range(copies - 1)]
     wqs = [wq0] + [wq0.clone() for _ in range(copies - 1)]
-    qs = [torch.empty((M, K), dtype=torch.uint8 if fp8 else torch.int8, device=dev) for _ in range(copies)]
+    qs = [torch.empty((lib.packed_bytes(M, K),), dtype=torch.uint8 if fp8 else torch.int8, device=dev)
+          for _ in range(copies)]
     ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(copies)]
     ys = [torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     torch.cuda.synchronize()
 
     L = lib._lib
     stream = torch.cuda.current_stream().cuda_stream
-    qfn = L.w8a8_quantize_act_fp8 if fp8 else L.w8a8_quantize_act
-    gfn = {"linear": L.w8a8_gemm_dequant, "gateup": L.w8a8_gemm_swiglu, "fp8": L.w8a8_fp8_gemm_dequant}[wl.kind]
+    qfn = L.w8a8_quantize_act_fp8_packed if fp8 else L.w8a8_quantize_act_packed
+    gfn = {"linear": L.w8a8_gemm_dequant_packed, "gateup": L.w8a8_gemm_swiglu_packed,
+           "fp8": L.w8a8_fp8_gemm_dequant_packed}[wl.kind]
     bptr = None if bias0 is None else bias0.data_ptr()
     sch = s_ch0.data_ptr()
     qargs = [(xs[i].data_ptr(), M, K, wl.rot_block, qs[i].data_ptr(), ss[i].data_ptr(), stream)

@@ -77,9 +77,31 @@ typedef enum {
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* w8a8_status_string(w8a8_status s);
 
+/* ---- packed operand layout ---------------------------------------------------
+ * A matrix of `rows` rows of K one-byte codes (K % 64 == 0) stored as blocks of
+ * 32 rows x 64 bytes: block (r / 32, k / 64) starts at byte
+ * ((r / 32) * (K / 64) + k / 64) * 2048 and holds row r % 32 of the block at
+ * byte 64 * (r % 32) within it.  The row count is rounded up to a multiple of
+ * 32.  Each 32-row, 64-byte piece of a GEMM stage is then one contiguous 2 KiB
+ * read.  Weights are immutable once loaded ("Loading CLEF INT8" page, as with
+ * the load-time gate/up packing), so a loader packs them once with
+ * w8a8_pack_weight and calls the *_packed whole-path entry points. */
+
+/* Bytes of the packed form of `rows` x K codes: ceil(rows / 32) * 32 * K
+ * (0 for rows <= 0 or K <= 0). */
+size_t w8a8_packed_bytes(int64_t rows, int64_t K);
+
+/* Row-major codes w [rows, K] (int8 or E4M3FN, any one-byte codes) -> the packed
+ * layout in w_packed (w8a8_packed_bytes(rows, K) bytes, caller-owned; padding
+ * rows are written as zeros).  K % 64 == 0, 64 <= K <= W8A8_MAX_K.  For the
+ * SwiGLU entry points pack the whole [2N, K] gate/up matrix in one call. */
+w8a8_status w8a8_pack_weight(const void* w, int64_t rows, int64_t K, void* w_packed,
+                             hipStream_t stream);
+
 /* Bytes of device workspace the whole-path entry points need for M tokens of
- * K features: the int8 (or E4M3FN) codes [M, K] followed by the fp32 scales [M],
- * each part starting on a 256-byte boundary.  Returns 0 for M <= 0 or K <= 0. */
+ * K features: the int8 (or E4M3FN) codes of x in the packed layout
+ * (w8a8_packed_bytes(M, K) bytes) followed by the fp32 scales [M], each part
+ * starting on a 256-byte boundary.  Returns 0 for M <= 0 or K <= 0. */
 size_t w8a8_workspace_bytes(int64_t M, int64_t K);
 
 /* ---- stage 1: per-row dynamic symmetric quantizer ----------------------------
@@ -96,6 +118,14 @@ w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int rot_b
                               int8_t* q, float* s_tok, hipStream_t stream);
 w8a8_status w8a8_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int rot_block,
                                   uint8_t* q, float* s_tok, hipStream_t stream);
+/* The same quantizers writing the codes in the packed layout (K % 64 == 0;
+ * q_packed holds w8a8_packed_bytes(M, K) bytes; its padding rows are left
+ * untouched).  One set of packed activation codes can feed several packed
+ * GEMMs -- e.g. projections that share their input. */
+w8a8_status w8a8_quantize_act_packed(const uint16_t* x, int64_t M, int64_t K, int rot_block,
+                                     int8_t* q_packed, float* s_tok, hipStream_t stream);
+w8a8_status w8a8_quantize_act_fp8_packed(const uint16_t* x, int64_t M, int64_t K, int rot_block,
+                                         uint8_t* q_packed, float* s_tok, hipStream_t stream);
 
 /* ---- stage 2 alone: acc[m][n] = sum_k q[m][k] * w[n][k], exact int32 ----------
  * The raw integer contraction (diagnostic / test entry point). acc is int32 [M, N]. */
@@ -127,11 +157,30 @@ w8a8_status w8a8_fp8_gemm_dequant(const uint8_t* q, const float* s_tok, const ui
                                   const float* s_ch, const uint16_t* bias, uint16_t* y,
                                   int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+/* ---- stages 2+3 on packed operands ---------------------------------------------
+ * w8a8_gemm_dequant / w8a8_gemm_swiglu / w8a8_fp8_gemm_dequant with both code
+ * matrices in the packed layout: q_packed from w8a8_quantize_act*_packed (M
+ * rows), the weight from w8a8_pack_weight (N rows, or 2N gate/up rows).  Same
+ * arithmetic and results as the row-major forms. */
+w8a8_status w8a8_gemm_dequant_packed(const int8_t* q_packed, const float* s_tok, const int8_t* w_packed,
+                                     const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
+                                     int64_t N, int64_t K, hipStream_t stream);
+w8a8_status w8a8_gemm_swiglu_packed(const int8_t* q_packed, const float* s_tok,
+                                    const int8_t* w_gateup_packed, const float* s_ch,
+                                    const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                    hipStream_t stream);
+w8a8_status w8a8_fp8_gemm_dequant_packed(const uint8_t* q_packed, const float* s_tok,
+                                         const uint8_t* w_packed, const float* s_ch,
+                                         const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
+                                         int64_t K, hipStream_t stream);
+
 /* ---- whole paths: quantize x into the workspace, then GEMM + epilogue --------
  * `workspace` must hold w8a8_workspace_bytes(M, K) bytes (256-byte aligned is
  * best; 16-byte aligned is required) and is used as scratch for the quantized
- * activations and their scales; its contents afterwards are those codes and
- * scales.  Two kernels are enqueued on `stream`. */
+ * activations and their scales; its contents afterwards are those codes (in
+ * the packed layout) and scales.  Two kernels are enqueued on `stream`.  The
+ * plain forms take the row-major weight; the *_packed forms take the weight
+ * as written by w8a8_pack_weight (same arithmetic, same results). */
 w8a8_status w8a8_linear(const uint16_t* x, const int8_t* w, const float* s_ch, const uint16_t* bias,
                         uint16_t* y, int64_t M, int64_t N, int64_t K, int rot_block,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
@@ -145,6 +194,21 @@ w8a8_status w8a8_fp8_linear(const uint16_t* x, const uint8_t* w, const float* s_
                             const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
                             int rot_block, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+w8a8_status w8a8_linear_packed(const uint16_t* x, const int8_t* w_packed, const float* s_ch,
+                               const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                               int rot_block, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
+
+w8a8_status w8a8_gateup_swiglu_packed(const uint16_t* x, const int8_t* w_gateup_packed,
+                                      const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
+                                      int64_t N, int64_t K, int rot_block, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream);
+
+w8a8_status w8a8_fp8_linear_packed(const uint16_t* x, const uint8_t* w_packed, const float* s_ch,
+                                   const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                   int rot_block, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -39,6 +39,16 @@ def lib():
         "w8a8_linear": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_gateup_swiglu": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_fp8_linear": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+        "w8a8_packed_bytes": (SZ, [I64, I64]),
+        "w8a8_pack_weight": (I, [P, I64, I64, P, P]),
+        "w8a8_quantize_act_packed": (I, [P, I64, I64, I, P, P, P]),
+        "w8a8_quantize_act_fp8_packed": (I, [P, I64, I64, I, P, P, P]),
+        "w8a8_gemm_dequant_packed": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_gemm_swiglu_packed": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_fp8_gemm_dequant_packed": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+        "w8a8_gateup_swiglu_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+        "w8a8_fp8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -55,7 +65,11 @@ def declared_symbols():
 def test_header_declares_the_documented_entry_points():
     want = {"w8a8_status_string", "w8a8_workspace_bytes", "w8a8_quantize_act",
             "w8a8_quantize_act_fp8", "w8a8_gemm_i32", "w8a8_gemm_dequant", "w8a8_gemm_swiglu",
-            "w8a8_fp8_gemm_dequant", "w8a8_linear", "w8a8_gateup_swiglu", "w8a8_fp8_linear"}
+            "w8a8_fp8_gemm_dequant", "w8a8_linear", "w8a8_gateup_swiglu", "w8a8_fp8_linear",
+            "w8a8_packed_bytes", "w8a8_pack_weight", "w8a8_linear_packed",
+            "w8a8_gateup_swiglu_packed", "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed",
+            "w8a8_quantize_act_fp8_packed", "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed",
+            "w8a8_fp8_gemm_dequant_packed"}
     assert want <= set(declared_symbols())
 
 
@@ -70,11 +84,17 @@ def test_status_strings(lib):
     assert b"unknown" in lib.w8a8_status_string(99)
 
 
-def test_workspace_bytes(lib):
+def test_packed_and_workspace_bytes(lib):
+    # packed codes: rows rounded up to a multiple of 32
+    assert lib.w8a8_packed_bytes(0, 128) == 0
+    assert lib.w8a8_packed_bytes(1, 128) == 32 * 128
+    assert lib.w8a8_packed_bytes(32, 4096) == 32 * 4096
+    assert lib.w8a8_packed_bytes(1502, 4096) == 1504 * 4096
+    # workspace: packed codes, then the fp32 scales, each on a 256-byte boundary
     assert lib.w8a8_workspace_bytes(0, 128) == 0
-    assert lib.w8a8_workspace_bytes(1, 128) == 256 + 256
-    assert lib.w8a8_workspace_bytes(12016, 17408) == 12016 * 17408 + ((12016 * 4 + 255) // 256) * 256
-    assert lib.w8a8_workspace_bytes(3, 16) % 256 == 0
+    assert lib.w8a8_workspace_bytes(1, 128) == 32 * 128 + 256
+    assert lib.w8a8_workspace_bytes(12016, 17408) == 12032 * 17408 + ((12016 * 4 + 255) // 256) * 256
+    assert lib.w8a8_workspace_bytes(3, 64) % 256 == 0
 
 
 def test_quantize_argument_checks(lib):
@@ -94,6 +114,11 @@ def test_quantize_argument_checks(lib):
     assert q(A, 0, 128, 0, A, A, None) == OK                 # M == 0: nothing enqueued
     assert lib.w8a8_quantize_act_fp8(A, 0, 256, 128, A, A, None) == OK
     assert lib.w8a8_quantize_act_fp8(A, 4, 200, 128, A, A, None) == SHAPE
+    for qp in (lib.w8a8_quantize_act_packed, lib.w8a8_quantize_act_fp8_packed):
+        assert qp(A, 4, 96, 0, A, A, None) == SHAPE          # packed codes need K % 64
+        assert qp(A, 4, 128, 0, None, A, None) == NULLP
+        assert qp(A, 4, 128, 0, U, A, None) == MISALIGNED
+        assert qp(A, 0, 64, 0, A, A, None) == OK
 
 
 def test_gemm_argument_checks(lib):
@@ -114,6 +139,11 @@ def test_gemm_argument_checks(lib):
     assert lib.w8a8_gemm_i32(A, A, A, 0, 8, 128, None) == OK
     assert lib.w8a8_gemm_swiglu(A, A, A, A, None, A, 4, 8, 100, None) == SHAPE
     assert lib.w8a8_fp8_gemm_dequant(A, A, A, A, None, A, 4, 8, 256, None) in (OK, DEVICE)
+    for gp in (lib.w8a8_gemm_dequant_packed, lib.w8a8_gemm_swiglu_packed, lib.w8a8_fp8_gemm_dequant_packed):
+        assert gp(None, A, A, A, None, A, 4, 8, 128, None) == NULLP
+        assert gp(A, A, A, A, None, A, 4, 8, 64, None) == SHAPE
+        assert gp(A, A, A, A, None, A, 4, 12, 128, None) == SHAPE
+        assert gp(A, A, A, A, None, A, 0, 8, 128, None) == OK
 
 
 def test_whole_path_argument_checks(lib):
@@ -128,6 +158,24 @@ def test_whole_path_argument_checks(lib):
     assert f(A, A, A, None, A, 0, 8, 256, 0, A, 0, None) == OK
     assert lib.w8a8_gateup_swiglu(A, A, A, None, A, 4, 8, 256, 128, A, ws - 256, None) == BADARG
     assert lib.w8a8_fp8_linear(A, A, None, None, A, 4, 8, 256, 0, A, ws, None) == NULLP
+    for g in (lib.w8a8_linear_packed, lib.w8a8_gateup_swiglu_packed, lib.w8a8_fp8_linear_packed):
+        assert g(A, None, A, None, A, 4, 8, 256, 0, A, ws, None) == NULLP
+        assert g(A, A, A, None, A, 4, 8, 256, 0, A, ws - 1, None) == BADARG
+        assert g(A, A, A, None, A, 4, 12, 256, 0, A, ws, None) == SHAPE
+        assert g(None, None, None, None, None, 0, 8, 256, 0, None, 0, None) == OK
+
+
+def test_pack_weight_argument_checks(lib):
+    p = lib.w8a8_pack_weight
+    assert p(None, 4, 128, A, None) == NULLP
+    assert p(A, 4, 128, None, None) == NULLP
+    assert p(A, 4, 96, A, None) == SHAPE          # K % 64
+    assert p(A, 4, 0, A, None) == SHAPE
+    assert p(A, -1, 128, A, None) == SHAPE
+    assert p(A, 4, 131072 + 64, A, None) == SHAPE
+    assert p(U, 4, 128, A, None) == MISALIGNED
+    assert p(A, 4, 128, U, None) == MISALIGNED
+    assert p(None, 0, 128, None, None) == OK      # nothing to pack
 
 
 def test_valid_call_without_gpu_reports_device(lib):
@@ -136,3 +184,4 @@ def test_valid_call_without_gpu_reports_device(lib):
         pytest.skip("a GPU is present; covered by the GPU tests")
     assert lib.w8a8_quantize_act(A, 4, 128, 0, A, A, None) == DEVICE
     assert lib.w8a8_gemm_i32(A, A, A, 4, 8, 128, None) == DEVICE
+    assert lib.w8a8_pack_weight(A, 4, 128, A, None) == DEVICE

@@ -1,12 +1,16 @@
 """GPU parity of the whole paths (quantize + GEMM + epilogue) against the CPU oracle.
 
 * Each of the five workloads at its full size, in the launch configuration the
-  benchmark times: the GPU quantizes the weight itself (compared with the
-  oracle's weight codes and scales, whole matrix), runs the whole path, and a
-  seeded sample of token rows (first/last rows, rows on tile boundaries) is
-  recomputed by the oracle one by one: activation codes and scales (read back
-  from the workspace) and every output column of those rows.
-* Smaller shapes compared on every element.
+  benchmark times (weight quantized on the GPU, packed once, whole path on the
+  packed weight): the weight codes and scales are compared with the oracle's
+  over the whole matrix, and a seeded sample of token rows (first/last rows,
+  rows on tile boundaries) is recomputed by the oracle one by one: activation
+  codes and scales (read back from the workspace, whose codes are in the
+  packed layout) and every output column of those rows.  The row-major-weight
+  entry point must give the same bytes.
+* Smaller shapes compared on every element, through both weight layouts; they
+  are chosen so that every tile configuration (128 x 128, 192 x 128 and
+  256 x 256) runs with each epilogue, with ragged M and N edges.
 * Properties that hold at any size: rows are byte-identical however the batch
   is split (row results must not depend on batching), repeated runs are
   byte-identical, and a non-default stream gives the same bytes.
@@ -34,6 +38,22 @@ def _gpu_path(lib, wl, x, wq, s_ch, bias, workspace=None, out=None):
     return fn(x, wq, s_ch, bias, rot_block=wl.rot_block, workspace=workspace, out=out)
 
 
+def _gpu_path_packed(lib, wl, x, wp, s_ch, bias, workspace=None, out=None):
+    fn = {"linear": lib.w8a8_linear_packed, "gateup": lib.w8a8_gateup_swiglu_packed,
+          "fp8": lib.w8a8_fp8_linear_packed}[wl.kind]
+    return fn(x, wp, wl.N, s_ch, bias, rot_block=wl.rot_block, workspace=workspace, out=out)
+
+
+def _unpack(flat: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Packed layout -> row-major [rows, K]: blocks of 32 rows x 64 bytes, block
+    (r // 32, k // 64) at byte ((r // 32) * (K // 64) + k // 64) * 2048, row r % 32
+    of the block at byte 64 * (r % 32) within it."""
+    r = np.arange(rows)[:, None]
+    k = np.arange(K)[None, :]
+    idx = ((r // 32) * (K // 64) + k // 64) * 2048 + (r % 32) * 64 + k % 64
+    return flat[idx]
+
+
 def _oracle_quant(orc, wl, a_bits):
     return orc.quantize_fp8(a_bits, wl.rot_block) if wl.kind == "fp8" else orc.quantize_i8(a_bits, wl.rot_block)
 
@@ -56,9 +76,14 @@ def _check_workload(lib, orc, wl, rows=None):
     x = inp.x.to(dev)
     bias = None if inp.bias is None else inp.bias.to(dev)
     wq, s_ch = quant(inp.w.to(dev), wl.rot_block)
+    wp = lib.w8a8_pack_weight(wq)
     ws = torch.empty(lib.workspace_bytes(wl.M, wl.K), dtype=torch.uint8, device=dev)
-    y = _gpu_path(lib, wl, x, wq, s_ch, bias, workspace=ws)
+    y = _gpu_path_packed(lib, wl, x, wp, s_ch, bias, workspace=ws)
     torch.cuda.synchronize()
+    codes_flat = ws.cpu().numpy()
+    y_rowmajor_w = _gpu_path(lib, wl, x, wq, s_ch, bias)
+    assert torch.equal(y_rowmajor_w, y), "row-major and packed weights give different outputs"
+    del y_rowmajor_w
 
     wq_ref, s_ch_ref = _oracle_quant(orc, wl, W.bits(inp.w))
     compare_codes(wq.cpu().numpy(), wq_ref, "weight codes")
@@ -67,9 +92,11 @@ def _check_workload(lib, orc, wl, rows=None):
     rows = np.arange(wl.M) if rows is None else rows
     x_rows = W.bits(inp.x)[rows]
     q_ref, s_ref = _oracle_quant(orc, wl, x_rows)
-    codes = ws[: wl.M * wl.K].view(wl.M, wl.K).cpu().numpy()
-    off = (wl.M * wl.K + 255) // 256 * 256
-    s_tok = ws[off: off + 4 * wl.M].view(torch.float32).cpu().numpy()
+    # workspace: packed codes (rows rounded up to 32), then the scales at the next 256-byte boundary
+    off = ((wl.M + 31) // 32 * 32 * wl.K + 255) // 256 * 256
+    assert lib.workspace_bytes(wl.M, wl.K) == off + (4 * wl.M + 255) // 256 * 256
+    codes = _unpack(codes_flat, wl.M, wl.K)
+    s_tok = codes_flat[off: off + 4 * wl.M].view(np.float32)
     compare_codes(codes[rows].view(np.uint8 if fp8 else np.int8), q_ref, "activation codes")
     assert np.array_equal(s_tok[rows].view(np.uint32), s_ref.view(np.uint32)), "activation scales"
 
@@ -95,6 +122,14 @@ SMALL = [
     W.custom("gateup", 257, 384, 72, 128, bias=True, seed=6),
     W.custom("fp8", 200, 512, 128, 0, bias=False, seed=7),
     W.custom("fp8", 131, 1024, 264, 128, bias=True, seed=8),
+    # 192 x 128 tiles (ragged M and N)
+    W.custom("linear", 1099, 256, 8184, 0, seed=21),
+    W.custom("gateup", 1099, 384, 4088, 128, seed=22),
+    W.custom("fp8", 1099, 256, 8184, 0, bias=True, seed=23),
+    # 256 x 256 tiles (ragged M and N; the gate/up up-row panel starts off a 32-row boundary)
+    W.custom("linear", 2047, 256, 8184, 128, seed=24),
+    W.custom("gateup", 2047, 256, 4088, 0, bias=True, seed=25),
+    W.custom("fp8", 2047, 384, 8184, 128, bias=False, seed=26),
 ]
 
 
@@ -129,3 +164,43 @@ def test_batch_split_invariance_and_determinism(lib, kind, rot):
     assert np.array_equal(b, bf16_bits(again)), "repeat run differs"
     assert np.array_equal(b, bf16_bits(torch.cat(pieces))), "batch split changes row results"
     assert np.array_equal(b, bf16_bits(other)), "non-default stream differs"
+
+
+@pytest.mark.parametrize("kind", ["linear", "fp8"])
+def test_batch_split_across_tile_configurations(lib, kind):
+    """2100 tokens run with 192 x 128 tiles, a 2048-token piece with 256 x 256
+    tiles and a 52-token piece with 128 x 128 tiles: the rows must agree byte
+    for byte (the k order of every output element is the same in all three)."""
+    wl = W.custom(kind, 2100, 256, 8192, 0, seed=12)
+    say(f"batch split across tile configurations {wl.name}")
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda")
+    quant = lib.w8a8_quantize_act_fp8 if kind == "fp8" else lib.w8a8_quantize_act
+    wq, s_ch = quant(inp.w.to(dev), 0)
+    wp = lib.w8a8_pack_weight(wq)
+    x = inp.x.to(dev)
+    bias = inp.bias.to(dev)
+    whole = _gpu_path_packed(lib, wl, x, wp, s_ch, bias)
+    a = _gpu_path_packed(lib, wl, x[:2048].contiguous(), wp, s_ch, bias)
+    b = _gpu_path_packed(lib, wl, x[2048:].contiguous(), wp, s_ch, bias)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(whole), bf16_bits(torch.cat([a, b]))), "tile configuration changes rows"
+
+
+@pytest.mark.parametrize("rows,K", [(1, 64), (31, 128), (32, 192), (100, 4096), (4097, 256)])
+def test_pack_weight_layout(lib, rows, K):
+    """w8a8_pack_weight writes the documented layout byte for byte, with zero padding rows."""
+    say(f"pack rows={rows} K={K}")
+    g = torch.Generator().manual_seed(rows * 7919 + K)
+    w = torch.randint(-128, 128, (rows, K), generator=g, dtype=torch.int8)
+    wp = lib.w8a8_pack_weight(w.to("cuda"))
+    torch.cuda.synchronize()
+    flat = wp.cpu().numpy()
+    prow = (rows + 31) // 32 * 32
+    assert flat.size == prow * K == lib.packed_bytes(rows, K)
+    wn = w.numpy()
+    assert np.array_equal(_unpack(flat, rows, K), wn)
+    assert np.array_equal(lib.unpack_rows(wp, rows, K).cpu().numpy(), wn)
+    if prow > rows:
+        pad = _unpack(flat, prow, K)[rows:]
+        assert not pad.any(), "padding rows must be zero"

@@ -185,3 +185,49 @@ def test_errors_surface_as_exceptions(lib):
     with pytest.raises(lib.W8A8Error) as e:
         lib.w8a8_quantize_act(xb, 0)
     assert e.value.status == 3
+
+
+def _unpack(flat: np.ndarray, rows: int, K: int) -> np.ndarray:
+    """Packed layout (blocks of 32 rows x 64 bytes, block (r // 32, k // 64) at byte
+    ((r // 32) * (K // 64) + k // 64) * 2048, row r % 32 at byte 64 * (r % 32) in
+    it) -> row-major [rows, K]."""
+    r = np.arange(rows)[:, None]
+    k = np.arange(K)[None, :]
+    return flat[((r // 32) * (K // 64) + k // 64) * 2048 + (r % 32) * 64 + k % 64]
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("M,K,rot", [(1, 64, 0), (33, 192, 0), (298, 1024, 128), (7, 17408, 0),
+                                     (65, 4096, 128), (2, 131072, 0)])
+def test_quantize_packed(lib, orc, fp8, M, K, rot):
+    """The packed-layout quantizer writes the oracle's codes at the packed addresses."""
+    say(f"quantize packed fp8={fp8} M={M} K={K} rot={rot}")
+    x = _x_case(M, K, rot, seed=300 + M + K, zero_rows=(1,))
+    qp, s = (lib.w8a8_quantize_act_fp8_packed if fp8 else lib.w8a8_quantize_act_packed)(x.cuda(), rot)
+    torch.cuda.synchronize()
+    q_ref, s_ref = (orc.quantize_fp8 if fp8 else orc.quantize_i8)(W.bits(x), rot)
+    got = _unpack(qp.cpu().numpy(), M, K)
+    (compare_codes_fp8 if fp8 else compare_codes_i8)(got, q_ref, "packed codes")
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "scales differ"
+
+
+@pytest.mark.parametrize("kind", ["dequant", "swiglu", "fp8"])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (130, 136, 256), (1099, 4088, 256), (2047, 4088, 384)])
+def test_gemm_stages_on_packed_operands(lib, orc, kind, M, N, K):
+    """Packed activation codes x packed weight codes through the *_packed GEMM entry
+    points, against the oracle (tile configurations 128, 192 and 256 all run)."""
+    say(f"packed gemm {kind} M={M} N={N} K={K}")
+    Nw = 2 * N if kind == "swiglu" else N
+    if kind == "fp8":
+        q, w = _fp8_codes((M, K), 51 + M), _fp8_codes((Nw, K), 53 + N)
+    else:
+        q, w = W.random_codes((M, K), seed=51 + M), W.random_codes((Nw, K), seed=53 + N)
+    s_tok, s_ch, b = _scales_bias(M, Nw, 57, bias=True)
+    qp, wp = lib.w8a8_pack_weight(q.cuda()), lib.w8a8_pack_weight(w.cuda())
+    fn = {"dequant": lib.w8a8_gemm_dequant_packed, "swiglu": lib.w8a8_gemm_swiglu_packed,
+          "fp8": lib.w8a8_fp8_gemm_dequant_packed}[kind]
+    y = fn(qp, s_tok.cuda(), wp, s_ch.cuda(), K, bias=b.cuda())
+    torch.cuda.synchronize()
+    ref_fn = {"dequant": orc.gemm_dequant, "swiglu": orc.gemm_swiglu, "fp8": orc.fp8_gemm_dequant}[kind]
+    ref = ref_fn(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), W.bits(b))
+    compare_bf16(bf16_bits(y), ref, "y")

@@ -22,10 +22,12 @@ from typing import Optional, Tuple
 import torch
 
 __all__ = [
-    "LIB_PATH", "W8A8Error", "workspace_bytes",
-    "w8a8_quantize_act", "w8a8_quantize_act_fp8", "w8a8_gemm_i32", "w8a8_gemm_dequant",
-    "w8a8_gemm_swiglu", "w8a8_fp8_gemm_dequant", "w8a8_linear", "w8a8_gateup_swiglu",
-    "w8a8_fp8_linear",
+    "LIB_PATH", "W8A8Error", "workspace_bytes", "packed_bytes", "unpack_rows",
+    "w8a8_pack_weight", "w8a8_quantize_act", "w8a8_quantize_act_fp8", "w8a8_gemm_i32",
+    "w8a8_gemm_dequant", "w8a8_gemm_swiglu", "w8a8_fp8_gemm_dequant", "w8a8_linear",
+    "w8a8_gateup_swiglu", "w8a8_fp8_linear", "w8a8_linear_packed", "w8a8_gateup_swiglu_packed",
+    "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed", "w8a8_quantize_act_fp8_packed",
+    "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed", "w8a8_fp8_gemm_dequant_packed",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
@@ -39,6 +41,8 @@ _P, _I64, _I, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size
 _SIGS = {
     "w8a8_status_string": (ctypes.c_char_p, [_I]),
     "w8a8_workspace_bytes": (_SZ, [_I64, _I64]),
+    "w8a8_packed_bytes": (_SZ, [_I64, _I64]),
+    "w8a8_pack_weight": (_I, [_P, _I64, _I64, _P, _P]),
     "w8a8_quantize_act": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "w8a8_quantize_act_fp8": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "w8a8_gemm_i32": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
@@ -48,6 +52,14 @@ _SIGS = {
     "w8a8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_gateup_swiglu": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_fp8_linear": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "w8a8_quantize_act_packed": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "w8a8_quantize_act_fp8_packed": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
+    "w8a8_gemm_dequant_packed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_gemm_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_fp8_gemm_dequant_packed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "w8a8_gateup_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "w8a8_fp8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -89,6 +101,34 @@ def workspace_bytes(M: int, K: int) -> int:
     return int(_lib.w8a8_workspace_bytes(M, K))
 
 
+def packed_bytes(rows: int, K: int) -> int:
+    return int(_lib.w8a8_packed_bytes(rows, K))
+
+
+def unpack_rows(packed: torch.Tensor, rows: int, K: int) -> torch.Tensor:
+    """View-and-copy inverse of the packed layout (32-row x 64-byte blocks) for
+    inspection: a flat byte tensor holding at least packed_bytes(rows, K) bytes
+    -> [rows, K] in row-major order, same dtype and device."""
+    n = packed_bytes(rows, K)
+    blocks = packed.reshape(-1)[:n].reshape(-1, K // 64, 32, 64)   # [row block, k block, row, byte]
+    return blocks.permute(0, 2, 1, 3).reshape(-1, K)[:rows].contiguous()
+
+
+def w8a8_pack_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Row-major one-byte codes w [rows, K] (int8 or uint8) -> flat packed copy
+    (packed_bytes(rows, K) elements of w's dtype)."""
+    if w.dtype not in (torch.int8, torch.uint8):
+        raise TypeError(f"w: expected int8 or uint8 codes, got {w.dtype}")
+    _want(w, w.dtype, "w", 2)
+    rows, K = w.shape
+    n = packed_bytes(rows, K)
+    wp = out if out is not None else torch.empty((max(n, 1),), dtype=w.dtype, device=w.device)
+    if wp.numel() < n:
+        raise ValueError("out is smaller than packed_bytes(rows, K)")
+    _check(_lib.w8a8_pack_weight(_ptr(w), rows, K, _ptr(wp), _stream()), "w8a8_pack_weight")
+    return wp
+
+
 # ---------------------------------------------------------------- stage 1 ----
 def w8a8_quantize_act(x: torch.Tensor, rot_block: int = 0,
                       out: Optional[Tuple[torch.Tensor, torch.Tensor]] = None):
@@ -112,6 +152,28 @@ def w8a8_quantize_act_fp8(x: torch.Tensor, rot_block: int = 0,
     _check(_lib.w8a8_quantize_act_fp8(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()),
            "w8a8_quantize_act_fp8")
     return q, s
+
+
+def _quant_packed(fname, x, rot_block, qdtype, out):
+    _want(x, torch.bfloat16, "x", 2)
+    M, K = x.shape
+    n = packed_bytes(M, K)
+    q, s = out if out is not None else (torch.empty((max(n, 1),), dtype=qdtype, device=x.device),
+                                        torch.empty((M,), dtype=torch.float32, device=x.device))
+    if q.numel() < n:
+        raise ValueError("q is smaller than packed_bytes(M, K)")
+    _check(getattr(_lib, fname)(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()), fname)
+    return q, s
+
+
+def w8a8_quantize_act_packed(x: torch.Tensor, rot_block: int = 0, out=None):
+    """Per-row int8 quantizer writing the packed layout: (q int8 flat, s fp32 [M])."""
+    return _quant_packed("w8a8_quantize_act_packed", x, rot_block, torch.int8, out)
+
+
+def w8a8_quantize_act_fp8_packed(x: torch.Tensor, rot_block: int = 0, out=None):
+    """Per-row E4M3FN quantizer writing the packed layout: (codes uint8 flat, s fp32 [M])."""
+    return _quant_packed("w8a8_quantize_act_fp8_packed", x, rot_block, torch.uint8, out)
 
 
 # ------------------------------------------------------------ stages 2, 3 ----
@@ -164,17 +226,60 @@ def w8a8_fp8_gemm_dequant(q, s_tok, w, s_ch, bias=None, out=None):
     return _epi("w8a8_fp8_gemm_dequant", q, s_tok, w, s_ch, bias, w.shape[0], torch.uint8, out)
 
 
+def _epi_packed(fname, q, s_tok, w, s_ch, bias, M, n_out, K, qdtype, out):
+    _want(q, qdtype, "q", 1)
+    _want(w, qdtype, "w", 1)
+    _want(s_tok, torch.float32, "s_tok", 1)
+    _want(s_ch, torch.float32, "s_ch", 1)
+    if bias is not None:
+        _want(bias, torch.bfloat16, "bias", 1)
+    rows = s_ch.shape[0]
+    if s_tok.shape[0] != M or q.numel() < packed_bytes(M, K) or w.numel() < packed_bytes(rows, K):
+        raise ValueError("inconsistent shapes")
+    if bias is not None and bias.shape[0] != rows:
+        raise ValueError("bias length must equal the weight's rows")
+    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=q.device)
+    _check(getattr(_lib, fname)(_ptr(q), _ptr(s_tok), _ptr(w), _ptr(s_ch), _ptr(bias), _ptr(y),
+                                M, n_out, K, _stream()), fname)
+    return y
+
+
+def w8a8_gemm_dequant_packed(q_packed, s_tok, w_packed, s_ch, K, bias=None, out=None):
+    """w8a8_gemm_dequant on packed operands; M = len(s_tok), N = len(s_ch)."""
+    return _epi_packed("w8a8_gemm_dequant_packed", q_packed, s_tok, w_packed, s_ch, bias,
+                       s_tok.shape[0], s_ch.shape[0], K, torch.int8, out)
+
+
+def w8a8_gemm_swiglu_packed(q_packed, s_tok, w_gateup_packed, s_ch, K, bias=None, out=None):
+    """w8a8_gemm_swiglu on packed operands; M = len(s_tok), N = len(s_ch) / 2."""
+    return _epi_packed("w8a8_gemm_swiglu_packed", q_packed, s_tok, w_gateup_packed, s_ch, bias,
+                       s_tok.shape[0], s_ch.shape[0] // 2, K, torch.int8, out)
+
+
+def w8a8_fp8_gemm_dequant_packed(q_packed, s_tok, w_packed, s_ch, K, bias=None, out=None):
+    """w8a8_fp8_gemm_dequant on packed operands; M = len(s_tok), N = len(s_ch)."""
+    return _epi_packed("w8a8_fp8_gemm_dequant_packed", q_packed, s_tok, w_packed, s_ch, bias,
+                       s_tok.shape[0], s_ch.shape[0], K, torch.uint8, out)
+
+
 # ------------------------------------------------------------ whole paths ----
-def _path(fname, x, w, s_ch, bias, rot_block, n_out, wdtype, workspace, out):
+def _path(fname, x, w, s_ch, bias, rot_block, n_out, wdtype, workspace, out, w_rows=None):
+    """w_rows is None for a row-major weight [rows, K]; for a packed weight (flat)
+    it is the weight's row count."""
     _want(x, torch.bfloat16, "x", 2)
-    _want(w, wdtype, "w", 2)
+    _want(w, wdtype, "w", 1 if w_rows is not None else 2)
     _want(s_ch, torch.float32, "s_ch", 1)
     if bias is not None:
         _want(bias, torch.bfloat16, "bias", 1)
     M, K = x.shape
-    if w.shape[1] != K or s_ch.shape[0] != w.shape[0]:
-        raise ValueError("inconsistent shapes")
-    if bias is not None and bias.shape[0] != w.shape[0]:
+    rows = w.shape[0] if w_rows is None else w_rows
+    if w_rows is None and w.shape[1] != K:
+        raise ValueError("x and w disagree on K")
+    if w_rows is not None and w.numel() < packed_bytes(w_rows, K):
+        raise ValueError("packed weight is smaller than packed_bytes(rows, K)")
+    if s_ch.shape[0] != rows:
+        raise ValueError("s_ch length must equal the weight's rows")
+    if bias is not None and bias.shape[0] != rows:
         raise ValueError("bias length must equal the weight's rows")
     need = workspace_bytes(M, K)
     if workspace is None:
@@ -199,3 +304,22 @@ def w8a8_gateup_swiglu(x, w_gateup, s_ch, bias=None, rot_block=0, workspace=None
 def w8a8_fp8_linear(x, w, s_ch, bias=None, rot_block=0, workspace=None, out=None):
     """y bf16 [M, N]: per-token E4M3FN quantization of x, fp8 GEMM, dequant."""
     return _path("w8a8_fp8_linear", x, w, s_ch, bias, rot_block, w.shape[0], torch.uint8, workspace, out)
+
+
+def w8a8_linear_packed(x, w_packed, N, s_ch, bias=None, rot_block=0, workspace=None, out=None):
+    """w8a8_linear with the weight [N, K] given in the packed layout (w8a8_pack_weight)."""
+    return _path("w8a8_linear_packed", x, w_packed, s_ch, bias, rot_block, N, torch.int8, workspace,
+                 out, w_rows=N)
+
+
+def w8a8_gateup_swiglu_packed(x, w_gateup_packed, N, s_ch, bias=None, rot_block=0, workspace=None,
+                              out=None):
+    """w8a8_gateup_swiglu with the [2N, K] gate/up weight given in the packed layout."""
+    return _path("w8a8_gateup_swiglu_packed", x, w_gateup_packed, s_ch, bias, rot_block, N, torch.int8,
+                 workspace, out, w_rows=2 * N)
+
+
+def w8a8_fp8_linear_packed(x, w_packed, N, s_ch, bias=None, rot_block=0, workspace=None, out=None):
+    """w8a8_fp8_linear with the E4M3FN weight [N, K] given in the packed layout."""
+    return _path("w8a8_fp8_linear_packed", x, w_packed, s_ch, bias, rot_block, N, torch.uint8,
+                 workspace, out, w_rows=N)

@@ -50,9 +50,10 @@ w8a8_status check_gemm_shape(int64_t M, int64_t N, int64_t K) {
 // Order of the checks everywhere: shapes and scalar arguments, then (for M > 0)
 // pointers and alignment, then the device.  M == 0 touches no memory, so it is
 // OK with any pointers once the shapes are legal.
-w8a8_status quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, bool fp8, void* q,
-                     float* s, hipStream_t stream) {
+w8a8_status quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, bool fp8, bool packed,
+                     void* q, float* s, hipStream_t stream) {
   if (M < 0 || K < 32 || K > W8A8_MAX_K || K % 32 != 0 || M > (int64_t)1 << 31) return W8A8_ERR_BAD_SHAPE;
+  if (packed && K % 64 != 0) return W8A8_ERR_BAD_SHAPE;
   if (rot_block != 0 && rot_block != 128) return W8A8_ERR_BAD_ARGUMENT;
   if (rot_block == 128 && K % 128 != 0) return W8A8_ERR_BAD_SHAPE;
   if (M == 0) return W8A8_OK;
@@ -60,12 +61,12 @@ w8a8_status quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, boo
   if (!aligned16(x) || !aligned16(q) || !aligned16(s)) return W8A8_ERR_MISALIGNED;
   w8a8_status st;
   if ((st = check_device()) != W8A8_OK) return st;
-  return launched(w8a8::launch_quantize(x, M, K, rot_block, fp8, q, s, stream));
+  return launched(w8a8::launch_quantize(x, M, K, rot_block, fp8, packed, q, s, stream));
 }
 
-w8a8_status gemm_epilogue(w8a8::Epi epi, bool fp8, const void* q, const float* s_tok, const void* w,
-                          const float* s_ch, const uint16_t* bias, void* y, int64_t M, int64_t N,
-                          int64_t K, hipStream_t stream) {
+w8a8_status gemm_epilogue(w8a8::Epi epi, bool fp8, bool packed, const void* q, const float* s_tok,
+                          const void* w, const float* s_ch, const uint16_t* bias, void* y, int64_t M,
+                          int64_t N, int64_t K, hipStream_t stream) {
   const bool needs_scales = epi != w8a8::Epi::kRawI32;
   w8a8_status st = check_gemm_shape(M, N, K);
   if (st != W8A8_OK) return st;
@@ -75,11 +76,13 @@ w8a8_status gemm_epilogue(w8a8::Epi epi, bool fp8, const void* q, const float* s
       (needs_scales && (!aligned16(s_tok) || !aligned16(s_ch))))
     return W8A8_ERR_MISALIGNED;
   if ((st = check_device()) != W8A8_OK) return st;
-  return launched(w8a8::launch_gemm(epi, fp8, q, s_tok, w, s_ch, bias, y, M, N, K, stream));
+  return launched(w8a8::launch_gemm(epi, fp8, packed, packed, q, s_tok, w, s_ch, bias, y, M, N, K, stream));
 }
 
-// Whole path: quantize x into the workspace, then the GEMM + epilogue.
-w8a8_status whole_path(w8a8::Epi epi, bool fp8, const uint16_t* x, const void* w, const float* s_ch,
+// Whole path: quantize x into the workspace (packed layout), then the GEMM +
+// epilogue against a row-major or packed weight.
+w8a8_status whole_path(w8a8::Epi epi, bool fp8, bool w_packed, const uint16_t* x, const void* w,
+                       const float* s_ch,
                        const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
                        int rot_block, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   w8a8_status st = check_gemm_shape(M, N, K);
@@ -93,10 +96,11 @@ w8a8_status whole_path(w8a8::Epi epi, bool fp8, const uint16_t* x, const void* w
     return W8A8_ERR_MISALIGNED;
   if ((st = check_device()) != W8A8_OK) return st;
   uint8_t* q = static_cast<uint8_t*>(workspace);
-  float* s_tok = reinterpret_cast<float*>(q + align256((size_t)M * (size_t)K));
-  st = launched(w8a8::launch_quantize(x, M, K, rot_block, fp8, q, s_tok, stream));
+  float* s_tok = reinterpret_cast<float*>(q + align256(w8a8_packed_bytes(M, K)));
+  st = launched(w8a8::launch_quantize(x, M, K, rot_block, fp8, /*packed=*/true, q, s_tok, stream));
   if (st != W8A8_OK) return st;
-  return launched(w8a8::launch_gemm(epi, fp8, q, s_tok, w, s_ch, bias, y, M, N, K, stream));
+  return launched(w8a8::launch_gemm(epi, fp8, /*packed_a=*/true, w_packed, q, s_tok, w, s_ch, bias, y,
+                                    M, N, K, stream));
 }
 
 }  // namespace
@@ -116,48 +120,98 @@ const char* w8a8_status_string(w8a8_status s) {
   return "W8A8 unknown status";
 }
 
+size_t w8a8_packed_bytes(int64_t rows, int64_t K) {
+  if (rows <= 0 || K <= 0) return 0;
+  return (size_t)w8a8::packed_rows(rows) * (size_t)K;
+}
+
 size_t w8a8_workspace_bytes(int64_t M, int64_t K) {
   if (M <= 0 || K <= 0) return 0;
-  return align256((size_t)M * (size_t)K) + align256((size_t)M * sizeof(float));
+  return align256(w8a8_packed_bytes(M, K)) + align256((size_t)M * sizeof(float));
+}
+
+w8a8_status w8a8_pack_weight(const void* w, int64_t rows, int64_t K, void* w_packed,
+                             hipStream_t stream) {
+  if (rows < 0 || K < 64 || K > W8A8_MAX_K || K % 64 != 0 || rows > (int64_t)1 << 31)
+    return W8A8_ERR_BAD_SHAPE;
+  if (rows == 0) return W8A8_OK;
+  if (!w || !w_packed) return W8A8_ERR_NULL_POINTER;
+  if (!aligned16(w) || !aligned16(w_packed)) return W8A8_ERR_MISALIGNED;
+  w8a8_status st;
+  if ((st = check_device()) != W8A8_OK) return st;
+  return launched(w8a8::launch_pack_rows(w, rows, K, w_packed, stream));
 }
 
 w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int rot_block, int8_t* q,
                               float* s_tok, hipStream_t stream) {
-  return quantize(x, M, K, rot_block, false, q, s_tok, stream);
+  return quantize(x, M, K, rot_block, false, false, q, s_tok, stream);
 }
 
 w8a8_status w8a8_quantize_act_fp8(const uint16_t* x, int64_t M, int64_t K, int rot_block,
                                   uint8_t* q, float* s_tok, hipStream_t stream) {
-  return quantize(x, M, K, rot_block, true, q, s_tok, stream);
+  return quantize(x, M, K, rot_block, true, false, q, s_tok, stream);
+}
+
+w8a8_status w8a8_quantize_act_packed(const uint16_t* x, int64_t M, int64_t K, int rot_block,
+                                     int8_t* q_packed, float* s_tok, hipStream_t stream) {
+  return quantize(x, M, K, rot_block, false, true, q_packed, s_tok, stream);
+}
+
+w8a8_status w8a8_quantize_act_fp8_packed(const uint16_t* x, int64_t M, int64_t K, int rot_block,
+                                         uint8_t* q_packed, float* s_tok, hipStream_t stream) {
+  return quantize(x, M, K, rot_block, true, true, q_packed, s_tok, stream);
 }
 
 w8a8_status w8a8_gemm_i32(const int8_t* q, const int8_t* w, int32_t* acc, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream) {
-  return gemm_epilogue(w8a8::Epi::kRawI32, false, q, nullptr, w, nullptr, nullptr, acc, M, N, K, stream);
+  return gemm_epilogue(w8a8::Epi::kRawI32, false, false, q, nullptr, w, nullptr, nullptr, acc, M, N, K, stream);
 }
 
 w8a8_status w8a8_gemm_dequant(const int8_t* q, const float* s_tok, const int8_t* w, const float* s_ch,
                               const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream) {
-  return gemm_epilogue(w8a8::Epi::kDequant, false, q, s_tok, w, s_ch, bias, y, M, N, K, stream);
+  return gemm_epilogue(w8a8::Epi::kDequant, false, false, q, s_tok, w, s_ch, bias, y, M, N, K, stream);
 }
 
 w8a8_status w8a8_gemm_swiglu(const int8_t* q, const float* s_tok, const int8_t* w_gateup,
                              const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
                              int64_t N, int64_t K, hipStream_t stream) {
-  return gemm_epilogue(w8a8::Epi::kSwiglu, false, q, s_tok, w_gateup, s_ch, bias, y, M, N, K, stream);
+  return gemm_epilogue(w8a8::Epi::kSwiglu, false, false, q, s_tok, w_gateup, s_ch, bias, y, M, N, K, stream);
 }
 
 w8a8_status w8a8_fp8_gemm_dequant(const uint8_t* q, const float* s_tok, const uint8_t* w,
                                   const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
                                   int64_t N, int64_t K, hipStream_t stream) {
-  return gemm_epilogue(w8a8::Epi::kDequant, true, q, s_tok, w, s_ch, bias, y, M, N, K, stream);
+  return gemm_epilogue(w8a8::Epi::kDequant, true, false, q, s_tok, w, s_ch, bias, y, M, N, K, stream);
+}
+
+w8a8_status w8a8_gemm_dequant_packed(const int8_t* q_packed, const float* s_tok, const int8_t* w_packed,
+                                     const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
+                                     int64_t N, int64_t K, hipStream_t stream) {
+  return gemm_epilogue(w8a8::Epi::kDequant, false, true, q_packed, s_tok, w_packed, s_ch, bias, y, M, N,
+                       K, stream);
+}
+
+w8a8_status w8a8_gemm_swiglu_packed(const int8_t* q_packed, const float* s_tok,
+                                    const int8_t* w_gateup_packed, const float* s_ch,
+                                    const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                    hipStream_t stream) {
+  return gemm_epilogue(w8a8::Epi::kSwiglu, false, true, q_packed, s_tok, w_gateup_packed, s_ch, bias, y,
+                       M, N, K, stream);
+}
+
+w8a8_status w8a8_fp8_gemm_dequant_packed(const uint8_t* q_packed, const float* s_tok,
+                                         const uint8_t* w_packed, const float* s_ch,
+                                         const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
+                                         int64_t K, hipStream_t stream) {
+  return gemm_epilogue(w8a8::Epi::kDequant, true, true, q_packed, s_tok, w_packed, s_ch, bias, y, M, N,
+                       K, stream);
 }
 
 w8a8_status w8a8_linear(const uint16_t* x, const int8_t* w, const float* s_ch, const uint16_t* bias,
                         uint16_t* y, int64_t M, int64_t N, int64_t K, int rot_block, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
-  return whole_path(w8a8::Epi::kDequant, false, x, w, s_ch, bias, y, M, N, K, rot_block, workspace,
+  return whole_path(w8a8::Epi::kDequant, false, false, x, w, s_ch, bias, y, M, N, K, rot_block, workspace,
                     workspace_bytes, stream);
 }
 
@@ -165,7 +219,7 @@ w8a8_status w8a8_gateup_swiglu(const uint16_t* x, const int8_t* w_gateup, const 
                                const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
                                int rot_block, void* workspace, size_t workspace_bytes,
                                hipStream_t stream) {
-  return whole_path(w8a8::Epi::kSwiglu, false, x, w_gateup, s_ch, bias, y, M, N, K, rot_block,
+  return whole_path(w8a8::Epi::kSwiglu, false, false, x, w_gateup, s_ch, bias, y, M, N, K, rot_block,
                     workspace, workspace_bytes, stream);
 }
 
@@ -173,8 +227,32 @@ w8a8_status w8a8_fp8_linear(const uint16_t* x, const uint8_t* w, const float* s_
                             const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
                             int rot_block, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  return whole_path(w8a8::Epi::kDequant, true, x, w, s_ch, bias, y, M, N, K, rot_block, workspace,
+  return whole_path(w8a8::Epi::kDequant, true, false, x, w, s_ch, bias, y, M, N, K, rot_block, workspace,
                     workspace_bytes, stream);
+}
+
+w8a8_status w8a8_linear_packed(const uint16_t* x, const int8_t* w_packed, const float* s_ch,
+                               const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                               int rot_block, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  return whole_path(w8a8::Epi::kDequant, false, true, x, w_packed, s_ch, bias, y, M, N, K, rot_block,
+                    workspace, workspace_bytes, stream);
+}
+
+w8a8_status w8a8_gateup_swiglu_packed(const uint16_t* x, const int8_t* w_gateup_packed,
+                                      const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
+                                      int64_t N, int64_t K, int rot_block, void* workspace,
+                                      size_t workspace_bytes, hipStream_t stream) {
+  return whole_path(w8a8::Epi::kSwiglu, false, true, x, w_gateup_packed, s_ch, bias, y, M, N, K,
+                    rot_block, workspace, workspace_bytes, stream);
+}
+
+w8a8_status w8a8_fp8_linear_packed(const uint16_t* x, const uint8_t* w_packed, const float* s_ch,
+                                   const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
+                                   int rot_block, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  return whole_path(w8a8::Epi::kDequant, true, true, x, w_packed, s_ch, bias, y, M, N, K, rot_block,
+                    workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

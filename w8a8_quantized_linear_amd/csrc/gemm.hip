@@ -13,9 +13,9 @@
 //
 // Design.  Both operands are K-contiguous ("NT"), so MFMA operands load with no
 // transpose.  A workgroup of WGM x WGN waves owns a BM (tokens) x BN (weight
-// rows) tile; each wave accumulates a (BM/WGM) x (BN/WGN) sub-tile from 16x16
-// MFMA blocks: v_mfma_i32_16x16x64_i8 for int8; E4M3FN operands are widened
-// exactly to bf16 in registers and go through v_mfma_f32_16x16x32_bf16, because
+// rows) tile; each wave accumulates a (BM/WGM) x (BN/WGN) sub-tile from 32x32
+// MFMA blocks: v_mfma_i32_32x32x32_i8 for int8; E4M3FN operands are widened
+// exactly to bf16 in registers and go through v_mfma_f32_32x32x16_bf16, because
 // the gfx950 fp8 MFMAs sum groups of products at roughly 14-bit precision
 // (measured: error ~2e-4 of the output rms at K = 4096 whatever the instruction
 // width or accumulator chaining) -- not the fp32 accumulation the fp8 scheme
@@ -25,14 +25,14 @@
 // one token row.
 //
 // Per-wave LDS traffic is (rows_m + rows_n) x K bytes for 2 rows_m rows_n K
-// ops, so the large 128 x 128 wave tiles of the 256 x 256 configuration need
-// half the LDS bandwidth per MFMA of 64 x 64 tiles.  K advances 64 bytes per
-// stage through a ring of kStages LDS buffers filled by direct-to-LDS loads
-// (global_load_lds_dwordx4: no staging registers, no LDS write instructions),
-// issued kStages - 1 stages ahead of use; one barrier per stage.  LDS rows are XOR-swizzled in 16-byte
-// units so the MFMA operand reads are bank-conflict free.  Rows past M or past
-// the weight's rows re-read the last valid row; they only reach outputs that
-// are never stored.
+// ops, so large wave tiles need less LDS bandwidth per MFMA.  K advances BK = 64
+// bytes per stage through a ring of NST LDS buffers filled by direct-to-LDS
+// loads (global_load_lds_dwordx4: no staging registers, no LDS write
+// instructions), issued NST - 1 stages ahead of use; one barrier per stage.
+// LDS rows are XOR-swizzled in 16-byte units so the MFMA operand reads are
+// bank-conflict free.  Operands may be row-major or in the packed layout of
+// 32-row x 64-byte blocks, in which every 32 rows of a stage are one contiguous
+// 2 KiB read instead of 32 separate 64-byte pieces.
 //
 // Tile order: the hardware deals workgroups round-robin to the 8 XCDs (each
 // with its own L2), so block ids are remapped to give every XCD a contiguous
@@ -57,6 +57,7 @@ typedef __bf16 v4bf __attribute__((ext_vector_type(4)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr int kXcds = 8;
+constexpr int kCus = 256;
 constexpr int kGroupM = 4;
 
 // 16-byte chunk c of LDS row r (CH chunks per row) is stored at chunk position
@@ -137,7 +138,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
           const uint8_t* __restrict__ b, const float* __restrict__ s_ch,
@@ -172,28 +173,45 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   // Direct-to-LDS loads: each wave instruction fills 64 consecutive 16-byte LDS
   // slots; slot p of a stage holds chunk (p % CH) ^ swizzle of tile row p / CH,
   // so each lane fetches the global chunk that belongs in its slot.  Offsets
-  // are 32-bit and relative to the tile's panel; rows past M (or past the
-  // weight's rows) re-read the last valid row -- they only reach outputs never
-  // stored.
+  // are 32-bit and relative to a panel base that is uniform per load
+  // instruction; rows past M (or past the weight's rows) re-read the last valid
+  // row -- they only reach outputs never stored.  An operand is either
+  // row-major [rows][K] or packed (PA / PB): blocks of 32 rows x 64 bytes,
+  // block (r / 32, k / 64) at byte ((r / 32) * (K / 64) + k / 64) * 2048, so
+  // that each 32-row, 64-byte piece of a stage is one contiguous 2 KiB read.
+  // Panel bases are rows that are multiples of 32, at byte row * K in either
+  // layout.
+  auto src_off = [&](int64_t rel, int c, bool packed) -> uint32_t {
+    if (packed)
+      return (uint32_t)((rel / 32) * 32 * K + (rel % 32) * 64 + (c / 4) * 2048 + (c % 4) * 16);
+    return (uint32_t)(rel * K + c * 16);
+  };
+  constexpr int ROWS_PER_LOAD = NT / CH;
+  static_assert(EPI != Epi::kSwiglu || (BN / 2) % ROWS_PER_LOAD == 0,
+                "each load instruction reads gate rows only or up rows only");
   const uint8_t* a_panel = a + mb * K;
+  // SwiGLU: gate rows nb.. and up rows N + nb..; the up panel starts at the
+  // 32-row boundary at or below N + nb, so its relative rows start at up_skew.
+  const int64_t up_first = N + nb;
+  const int64_t up_base = PB ? up_first / 32 * 32 : up_first;
+  const int64_t up_skew = up_first - up_base;
   const uint8_t* b_panel = b + nb * K;
+  const uint8_t* b_up_panel = b + up_base * K;
   uint32_t a_off[A_LOADS], b_off[B_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
-    a_off[i] = (uint32_t)(min<int64_t>(r, M - 1 - mb) * K + c * 16);
+    a_off[i] = src_off(min<int64_t>(r, M - 1 - mb), c, PA);
   }
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
-    int64_t rel;  // weight row relative to nb
     if constexpr (EPI == Epi::kSwiglu) {
       const int64_t col = min<int64_t>(r % (BN / 2), N - 1 - nb);
-      rel = r < BN / 2 ? col : N + col;
+      b_off[i] = src_off(r < BN / 2 ? col : up_skew + col, c, PB);
     } else {
-      rel = min<int64_t>(r, N - 1 - nb);
+      b_off[i] = src_off(min<int64_t>(r, N - 1 - nb), c, PB);
     }
-    b_off[i] = (uint32_t)(rel * K + c * 16);
   }
   // Stages past the last one re-load the last stage into a buffer nobody reads
   // again, so every stage issues the same number of loads (constant vmcnt
@@ -202,13 +220,19 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   auto issue = [&](int64_t step) __attribute__((always_inline)) {
     // 32-bit per-stage offsets off a uniform panel base: the loads use the
     // scalar-base addressing form and keep one VGPR per load live, not two
-    const uint32_t k0 = (uint32_t)(min<int64_t>(step, ksteps - 1) * BK);
+    // (a stage of BK bytes advances BK bytes along a row-major row, or BK / 64
+    // blocks of 2 KiB in the packed layout)
+    const uint32_t ks = (uint32_t)min<int64_t>(step, ksteps - 1);
+    const uint32_t ka = PA ? ks * (BK / 64) * 2048 : ks * BK;
+    const uint32_t kb = PB ? ks * (BK / 64) * 2048 : ks * BK;
     uint8_t* st = lds + (int)(step % NST) * STAGE;
 #pragma unroll
-    for (int i = 0; i < A_LOADS; ++i) lds_dma16(a_panel + (a_off[i] + k0), st + (i * NT + wave * 64) * 16);
+    for (int i = 0; i < A_LOADS; ++i) lds_dma16(a_panel + (a_off[i] + ka), st + (i * NT + wave * 64) * 16);
 #pragma unroll
-    for (int i = 0; i < B_LOADS; ++i)
-      lds_dma16(b_panel + (b_off[i] + k0), st + A_BYTES + (i * NT + wave * 64) * 16);
+    for (int i = 0; i < B_LOADS; ++i) {
+      const bool up = EPI == Epi::kSwiglu && i * ROWS_PER_LOAD >= BN / 2;  // compile-time per i
+      lds_dma16((up ? b_up_panel : b_panel) + (b_off[i] + kb), st + A_BYTES + (i * NT + wave * 64) * 16);
+    }
   };
 
   using Acc = typename std::conditional<FP8, v16f, v16i>::type;
@@ -401,7 +425,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8>
+template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
 hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const float* s_ch,
                       const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
                       hipStream_t stream) {
@@ -410,41 +434,96 @@ hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const fl
   const int64_t tiles_n = (N + cols_per_tile - 1) / cols_per_tile;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((gemm_tile<BM, BN, WGM, WGN, BK, NST, EPI, FP8>), dim3((unsigned)blocks),
+  hipLaunchKernelGGL((gemm_tile<BM, BN, WGM, WGN, BK, NST, EPI, FP8, PA, PB>), dim3((unsigned)blocks),
                      dim3(64 * WGM * WGN), 0, stream, static_cast<const uint8_t*>(a), s_tok,
                      static_cast<const uint8_t*>(b), s_ch, bias, out, M, N, K, (int)tiles_m,
                      (int)tiles_n);
   return hipGetLastError();
 }
 
-// Tile choice: 256 x 256 (8 waves of 128 x 64) when it still fills the chip,
-// 128 x 128 (4 waves of 64 x 64) for small problems.
-template <Epi EPI, bool FP8>
+// Tile choice.  Candidates (all 4 waves, BK = 64, 4 stages):
+//   256 x 256: waves of 128 x 128, 128 KiB LDS, one workgroup per CU;
+//   192 x 128: waves of  96 x  64,  80 KiB LDS, two per CU;
+//   128 x 128: waves of  64 x  64,  64 KiB LDS, two per CU.
+// The kernel is throughput-bound per CU, so the time of a launch is taken as
+// (tiles per CU, rounded up) x (tile area) / (relative efficiency of the tile
+// shape); the efficiencies are the ops per CU-second of each shape relative to
+// 256 x 256, measured on 12,016 x 5,120 x 17,408 (0.90 and 0.80).  Ties go to
+// the larger tile.
+template <Epi EPI, bool FP8, bool PA, bool PB>
 hipError_t launch_t(const void* a, const float* s_tok, const void* b, const float* s_ch,
                     const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream) {
   const int64_t nw = (EPI == Epi::kSwiglu) ? 2 * N : N;  // weight rows
-  const int64_t big_tiles = ((M + 255) / 256) * ((nw + 255) / 256);
-  if (big_tiles >= 256)
-    return launch_cfg<256, 256, 2, 2, 64, 4, EPI, FP8>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
-  return launch_cfg<128, 128, 2, 2, 64, 4, EPI, FP8>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  auto cost = [&](int bm, int bn, double eff) {
+    const int64_t tiles = ((M + bm - 1) / bm) * ((nw + bn - 1) / bn);
+    return (double)((tiles + kCus - 1) / kCus) * bm * bn / eff;
+  };
+  const double c256 = cost(256, 256, 1.0), c192 = cost(192, 128, 0.90), c128 = cost(128, 128, 0.80);
+  if (c256 <= c192 && c256 <= c128)
+    return launch_cfg<256, 256, 2, 2, 64, 4, EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  if (c192 <= c128)
+    return launch_cfg<192, 128, 2, 2, 64, 4, EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  return launch_cfg<128, 128, 2, 2, 64, 4, EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+}
+
+template <Epi EPI, bool FP8>
+hipError_t launch_layouts(bool pa, bool pb, const void* a, const float* s_tok, const void* b,
+                          const float* s_ch, const uint16_t* bias, void* out, int64_t M, int64_t N,
+                          int64_t K, hipStream_t stream) {
+  if (!pa && !pb) return launch_t<EPI, FP8, false, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  if (pa && !pb) return launch_t<EPI, FP8, true, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  if (pa && pb) return launch_t<EPI, FP8, true, true>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  return hipErrorInvalidValue;
+}
+
+// Row-major [rows][K] -> packed blocks of 32 rows x 64 bytes (rows past `rows`
+// in the last block are zero).  One thread per 16 destination bytes, so the
+// writes are contiguous.
+__global__ void __launch_bounds__(256)
+pack_rows_kernel(const uint8_t* __restrict__ src, int64_t rows, int64_t K, uint8_t* __restrict__ dst,
+                 int64_t chunks) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= chunks) return;
+  const int64_t d = j * 16;
+  const int64_t block = d / 2048, within = d % 2048;
+  const int64_t kblocks = K / 64;
+  const int64_t row = (block / kblocks) * 32 + within / 64;
+  const int64_t k = (block % kblocks) * 64 + within % 64;
+  u32x4 v = u32x4{0, 0, 0, 0};
+  if (row < rows) v = *reinterpret_cast<const u32x4*>(src + row * K + k);
+  *reinterpret_cast<u32x4*>(dst + d) = v;
 }
 
 }  // namespace
 
-hipError_t launch_gemm(Epi epi, bool fp8, const void* a, const float* s_tok, const void* b,
-                       const float* s_ch, const uint16_t* bias, void* out,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const void* a,
+                       const float* s_tok, const void* b, const float* s_ch, const uint16_t* bias,
+                       void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (fp8) {
-    if (epi == Epi::kDequant) return launch_t<Epi::kDequant, true>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+    if (epi == Epi::kDequant)
+      return launch_layouts<Epi::kDequant, true>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
     return hipErrorInvalidValue;
   }
   switch (epi) {
-    case Epi::kRawI32: return launch_t<Epi::kRawI32, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
-    case Epi::kDequant: return launch_t<Epi::kDequant, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
-    case Epi::kSwiglu: return launch_t<Epi::kSwiglu, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+    case Epi::kRawI32:
+      if (packed_a || packed_b) return hipErrorInvalidValue;
+      return launch_t<Epi::kRawI32, false, false, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+    case Epi::kDequant:
+      return launch_layouts<Epi::kDequant, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+    case Epi::kSwiglu:
+      return launch_layouts<Epi::kSwiglu, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
   }
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream) {
+  const int64_t chunks = packed_rows(rows) * K / 16;
+  const int64_t blocks = (chunks + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack_rows_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(src), rows, K, static_cast<uint8_t*>(dst), chunks);
+  return hipGetLastError();
 }
 
 }  // namespace w8a8

@@ -10,14 +10,22 @@ namespace w8a8 {
 // Epilogues of the GEMM kernel.
 enum class Epi : int { kRawI32 = 0, kDequant = 1, kSwiglu = 2 };
 
-// Quantizer: rows of x [M, K] bf16 -> codes [M, K] (int8 or E4M3FN) + fp32 scale [M].
-hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, bool fp8,
-                           void* q, float* s, hipStream_t stream);
+// Packed operand layout: blocks of 32 rows x 64 bytes, block (r / 32, k / 64) at
+// byte ((r / 32) * (K / 64) + k / 64) * 2048, row r % 32 of the block at + 64 * (r % 32).
+inline int64_t packed_rows(int64_t rows) { return (rows + 31) / 32 * 32; }
 
-// GEMM + epilogue.  a: codes [M, K]; b: codes [Nw, K] (Nw = N, or 2N for SwiGLU);
-// out: int32 [M, N] or bf16 [M, N].
-hipError_t launch_gemm(Epi epi, bool fp8, const void* a, const float* s_tok, const void* b,
-                       const float* s_ch, const uint16_t* bias, void* out,
-                       int64_t M, int64_t N, int64_t K, hipStream_t stream);
+// Quantizer: rows of x [M, K] bf16 -> codes [M, K] (int8 or E4M3FN; row-major, or
+// packed when `packed`) + fp32 scale [M].
+hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, bool fp8,
+                           bool packed, void* q, float* s, hipStream_t stream);
+
+// GEMM + epilogue.  a: codes [M, K]; b: codes [Nw, K] (Nw = N, or 2N for SwiGLU),
+// each row-major or packed; out: int32 [M, N] or bf16 [M, N].
+hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const void* a,
+                       const float* s_tok, const void* b, const float* s_ch, const uint16_t* bias,
+                       void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+// Row-major codes [rows, K] -> packed layout (K % 64 == 0; padding rows zero).
+hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream);
 
 }  // namespace w8a8

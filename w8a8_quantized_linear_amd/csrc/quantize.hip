@@ -27,7 +27,10 @@
 //     a few ulps of a half-integer; those rare elements are redone with the
 //     IEEE division.  E4M3FN codes use the IEEE division and the hardware RNE
 //     converter after clamping to +-448.
-//   * 8-byte stores of the codes (contiguous across the wave without rotation).
+//   * 8-byte stores of the codes, row-major or in the GEMM's packed layout
+//     (blocks of 32 rows x 64 bytes, block (r / 32, k / 64) at byte
+//     ((r / 32) * (K / 64) + k / 64) * 2048); an 8-byte piece never straddles
+//     a 64-byte group, so the packed form only changes the address.
 #include "internal.h"
 
 namespace w8a8 {
@@ -83,7 +86,7 @@ constexpr int rows_per_block() { return (T < 256 && 256 % T == 0) ? 256 / T : 1;
 template <int T, int CMAX, bool ROT, bool FP8>
 __global__ void __launch_bounds__(T * rows_per_block<T>())
 quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restrict__ q,
-              float* __restrict__ s_out) {
+              float* __restrict__ s_out, bool packed) {
   constexpr int kRowsPerBlock = rows_per_block<T>();
   constexpr int kWavesPerRow = T / 64;
   const int tid = threadIdx.x % T;
@@ -183,7 +186,9 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
   const bool zero_row = !(amax > 0.0f);
   const float r = zero_row ? 0.0f : 1.0f / s;
 
-  uint8_t* qr = q + row * (int64_t)K;
+  // element e of this row (e % 8 == 0) goes to qr + (e & ~63) * kstride + (e & 63)
+  uint8_t* qr = q + (packed ? (row / 32) * 32 * (int64_t)K + (row % 32) * 64 : row * (int64_t)K);
+  const int kstride = packed ? 32 : 1;
 #pragma unroll
   for (int i = 0; i < CMAX; ++i) {
 #pragma unroll
@@ -212,21 +217,21 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
           out[g] = pack_i8x4(t[0], t[1], t[2], t[3]);
         }
       }
-      *reinterpret_cast<u32x2*>(qr + e0) = u32x2{out[0], out[1]};
+      *reinterpret_cast<u32x2*>(qr + ((e0 & ~63) * kstride + (e0 & 63))) = u32x2{out[0], out[1]};
     }
   }
 }
 
 template <int T, bool ROT, bool FP8>
 hipError_t dispatch_cmax(int cmax, const uint16_t* x, int64_t M, int K, uint8_t* q, float* s,
-                         hipStream_t stream) {
+                         bool packed, hipStream_t stream) {
   constexpr int kRowsPerBlock = rows_per_block<T>();
   const dim3 block(T * kRowsPerBlock);
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
   switch (cmax) {
 #define W8A8_Q_CASE(C)                                                                     \
   case C:                                                                                  \
-    hipLaunchKernelGGL((quantize_rows<T, C, ROT, FP8>), grid, block, 0, stream, x, M, K, q, s); \
+    hipLaunchKernelGGL((quantize_rows<T, C, ROT, FP8>), grid, block, 0, stream, x, M, K, q, s, packed); \
     break;
     W8A8_Q_CASE(1) W8A8_Q_CASE(2) W8A8_Q_CASE(3) W8A8_Q_CASE(4)
 #undef W8A8_Q_CASE
@@ -240,13 +245,13 @@ hipError_t dispatch_cmax(int cmax, const uint16_t* x, int64_t M, int K, uint8_t*
 // fewest lanes with at most 4 chunks per lane; rows longer than 4 x 256 chunks
 // (K > 32768) use 1024 threads.
 template <bool ROT, bool FP8>
-hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float* s,
+hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float* s, bool packed,
                          hipStream_t stream) {
   const int nchunks = K / kEPL;
   if (nchunks > 4 * 256) {
     const int cmax = (nchunks + 1023) / 1024;
     if (cmax > 4) return hipErrorInvalidValue;
-    return dispatch_cmax<1024, ROT, FP8>(cmax, x, M, K, q, s, stream);
+    return dispatch_cmax<1024, ROT, FP8>(cmax, x, M, K, q, s, packed, stream);
   }
   int best_t = 256, best_slots = 1 << 30;
   for (int t = 64; t <= 256; t += 64) {
@@ -256,25 +261,26 @@ hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float*
   }
   const int cmax = (nchunks + best_t - 1) / best_t;
   switch (best_t) {
-    case 64: return dispatch_cmax<64, ROT, FP8>(cmax, x, M, K, q, s, stream);
-    case 128: return dispatch_cmax<128, ROT, FP8>(cmax, x, M, K, q, s, stream);
-    case 192: return dispatch_cmax<192, ROT, FP8>(cmax, x, M, K, q, s, stream);
-    default: return dispatch_cmax<256, ROT, FP8>(cmax, x, M, K, q, s, stream);
+    case 64: return dispatch_cmax<64, ROT, FP8>(cmax, x, M, K, q, s, packed, stream);
+    case 128: return dispatch_cmax<128, ROT, FP8>(cmax, x, M, K, q, s, packed, stream);
+    case 192: return dispatch_cmax<192, ROT, FP8>(cmax, x, M, K, q, s, packed, stream);
+    default: return dispatch_cmax<256, ROT, FP8>(cmax, x, M, K, q, s, packed, stream);
   }
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int rot_block, bool fp8,
-                           void* q, float* s, hipStream_t stream) {
+                           bool packed, void* q, float* s, hipStream_t stream) {
   uint8_t* qb = static_cast<uint8_t*>(q);
   const int k = (int)K;
+  if (packed && K % 64 != 0) return hipErrorInvalidValue;
   if (rot_block == 128) {
-    return fp8 ? dispatch_rows<true, true>(x, M, k, qb, s, stream)
-               : dispatch_rows<true, false>(x, M, k, qb, s, stream);
+    return fp8 ? dispatch_rows<true, true>(x, M, k, qb, s, packed, stream)
+               : dispatch_rows<true, false>(x, M, k, qb, s, packed, stream);
   }
-  return fp8 ? dispatch_rows<false, true>(x, M, k, qb, s, stream)
-             : dispatch_rows<false, false>(x, M, k, qb, s, stream);
+  return fp8 ? dispatch_rows<false, true>(x, M, k, qb, s, packed, stream)
+             : dispatch_rows<false, false>(x, M, k, qb, s, packed, stream);
 }
 
 }  // namespace w8a8
