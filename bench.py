@@ -51,6 +51,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
+                    help="gate/up workloads: paired SwiGLU epilogue (fused) or the fuse_mlp=False "
+                         "chain -- GEMM onto the 2N packed rows with the dequant epilogue, then "
+                         "w8a8_swiglu (unfused)")
+    ap.add_argument("--drift", action="store_true",
+                    help="instead of timing: relative L2 drift of every workload's W8A8 output from "
+                         "the fp64 unquantized projection, without and with the block rotation")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="summarize rocprofv3 FETCH_SIZE / WRITE_SIZE runs of this script into "
                          "profiles/traffic_<workload>.json and exit")
@@ -123,7 +130,7 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
-def cpu_baseline(wl, inp):
+def cpu_baseline(wl, inp, unfused=False):
     """The CPU oracle, as it stands, on the whole workload (all rows), on this host."""
     import numpy as np
     import oracle
@@ -136,7 +143,8 @@ def cpu_baseline(wl, inp):
     # bounded sample: all rows when the whole pass is cheap enough, else a row slice
     rows = wl.M if wl.M * wl.n_w * wl.K <= 60 * 10 ** 9 else max(1, int(60 * 10 ** 9 // (wl.n_w * wl.K)))
     xs = np.ascontiguousarray(x[:rows])
-    fn = {"linear": oracle.linear, "gateup": oracle.gateup_swiglu, "fp8": oracle.fp8_linear}[wl.kind]
+    fn = {"linear": oracle.linear, "gateup": oracle.gateup_unfused if unfused else oracle.gateup_swiglu,
+          "fp8": oracle.fp8_linear}[wl.kind]
     t0 = time.perf_counter()
     fn(xs, wq, s_ch, bias, wl.rot_block, threads)
     dt = time.perf_counter() - t0
@@ -164,6 +172,23 @@ def main():
     import workloads as W
     import w8a8_quantized_linear_amd as lib
 
+    if args.drift:
+        import numpy as np
+        from w8a8_quantized_linear_amd.drift import drift
+        for name in W.ORDER:
+            wl = W.WORKLOADS[name]
+            inp = W.make_inputs(wl)
+            rng = np.random.default_rng(wl.seed)
+            rows = np.unique(np.concatenate([[0, wl.M - 1], rng.choice(wl.M, size=min(wl.M, 62), replace=False)]))
+            t0 = time.perf_counter()
+            d = drift(inp.x, inp.w, inp.bias, wl.kind, (0, 128), rows)
+            print(json.dumps({"drift": "relative L2 vs fp64 unquantized projection", "workload": name,
+                              "kind": wl.kind, "workload_rot_block": wl.rot_block,
+                              "rows_compared": int(len(rows)),
+                              "rel_l2": {str(k): v for k, v in d.items()},
+                              "seconds": round(time.perf_counter() - t0, 2)}), flush=True)
+        return
+
     wl = W.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -174,6 +199,10 @@ def main():
     torch.add(calib_src, 1.0, out=calib_dst)
     torch.cuda.synchronize()
     del calib_src, calib_dst
+    unfused = args.path == "unfused"
+    if unfused and wl.kind != "gateup":
+        print("bench.py: --path unfused applies to gate/up workloads only", file=sys.stderr)
+        sys.exit(2)
     inp = W.make_inputs(wl)
     fp8 = wl.kind == "fp8"
     quant = lib.w8a8_quantize_act_fp8 if fp8 else lib.w8a8_quantize_act
@@ -194,6 +223,8 @@ def main():
           for _ in range(copies)]
     ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(copies)]
     ys = [torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    # unfused: the bf16 gate/up projection [M, 2N] between the GEMM and the SwiGLU pass
+    hs = [torch.empty((M, Nw), dtype=torch.bfloat16, device=dev) for _ in range(copies)] if unfused else []
     torch.cuda.synchronize()
 
     L = lib._lib
@@ -205,8 +236,16 @@ def main():
     sch = s_ch0.data_ptr()
     qargs = [(xs[i].data_ptr(), M, K, wl.rot_block, qs[i].data_ptr(), ss[i].data_ptr(), stream)
              for i in range(copies)]
-    gargs = [(qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(),
-              M, n_out, K, stream) for i in range(copies)]
+    if unfused:
+        gfn = L.w8a8_gemm_dequant_packed
+        gargs = [(qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, hs[i].data_ptr(),
+                  M, Nw, K, stream) for i in range(copies)]
+        sargs = [(hs[i].data_ptr(), hs[i].data_ptr() + 2 * n_out, Nw, ys[i].data_ptr(), M, n_out, stream)
+                 for i in range(copies)]
+    else:
+        gargs = [(qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(),
+                  M, n_out, K, stream) for i in range(copies)]
+    n_ev = 4 if unfused else 3
 
     def step(i, evs=None):
         c = i % copies
@@ -218,6 +257,10 @@ def main():
         st |= gfn(*gargs[c])
         if evs is not None:
             evs[2].record()
+        if unfused:
+            st |= L.w8a8_swiglu(*sargs[c])
+            if evs is not None:
+                evs[3].record()
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -237,7 +280,7 @@ def main():
     # kernel on the launch stream.  (Each event record is a command processor
     # packet that idles the GPU for a few microseconds between the kernels, so
     # it is kept out of the throughput measurement above.)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     for i in range(args.steps):
         step(i, evs[i])
@@ -248,9 +291,10 @@ def main():
     ms_per_step = wall / args.steps * 1e3
     ops = 2 * M * Nw * K
     q_bytes = 2 * M * K + M * K + 4 * M                      # read bf16 x, write codes + scales
-    g_bytes = M * K + Nw * K + 4 * (M + Nw) + M * n_out * 2 + (0 if bias0 is None else 2 * Nw)
+    out_cols = Nw if unfused else n_out                      # the unfused GEMM writes [M, 2N]
+    g_bytes = M * K + Nw * K + 4 * (M + Nw) + M * out_cols * 2 + (0 if bias0 is None else 2 * Nw)
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
-    traffic = stored_traffic(wl.name)
+    traffic = stored_traffic(wl.name + ("-unfused" if unfused else ""))
 
     out = {
         "metric": "W8A8 linear TOPS incl. quant+dequant, % int8 MFMA peak; quantizer GB/s",
@@ -266,7 +310,8 @@ def main():
         "dtype": "fp8-e4m3" if fp8 else "i8",
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": wl.name, "M": M, "K": K, "N": n_out, "weight_rows": Nw,
-                   "rot_block": wl.rot_block, "path": wl.kind, "parallelism": "single GPU",
+                   "rot_block": wl.rot_block, "path": wl.kind + ("-unfused" if unfused else ""),
+                   "parallelism": "single GPU",
                    "operand_copies": copies},
         "pct_of_peak": 100.0 * ops / (ms_per_step * 1e-3) / (peak * 1e12),
         "roofline": {"bound": "mfma", "achieved": ops / tg / 1e12, "peak": peak, "unit": "TFLOP/s",
@@ -277,8 +322,15 @@ def main():
                       "frac": q_bytes / tq / 1e9 / PEAK_HBM_GBS, "avg_launch_us": tq * 1e6,
                       "algorithmic_bytes": q_bytes},
     }
+    if unfused:
+        tsw = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+        sw_bytes = 6 * M * n_out                             # read gate + up, write y (bf16)
+        out["swiglu"] = {"bound": "hbm", "achieved": sw_bytes / tsw / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": sw_bytes / tsw / 1e9 / PEAK_HBM_GBS,
+                         "avg_launch_us": tsw * 1e6, "algorithmic_bytes": sw_bytes}
+        out["roofline"]["kernel"] = "gemm_tile (GEMM + dequant epilogue onto 2N columns)"
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, unfused)
     print(json.dumps(out), flush=True)
 
 

@@ -174,6 +174,19 @@ w8a8_status w8a8_fp8_gemm_dequant_packed(const uint8_t* q_packed, const float* s
                                          const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
                                          int64_t K, hipStream_t stream);
 
+/* ---- unfused gate/up: SwiGLU of separately projected gate and up -------------
+ * The "Loading CLEF INT8" page's fuse_mlp=False setting disables the paired
+ * gate/up epilogue: gate and up are then ordinary linears (for example one
+ * w8a8_linear onto the 2N packed rows, giving [M, 2N]) and this call combines
+ * their bf16 outputs: y[m][n] = bf16( silu(gate[m][n]) * up[m][n] ), evaluated
+ * in fp32 (g / (1 + exp(-g)) * u) with one round to nearest even.  gate and up
+ * are bf16 [M, N] whose rows are `ld` elements apart (ld >= N; ld = 2N and
+ * up = gate + N for the halves of a [M, 2N] projection); y is dense [M, N].
+ * N % 8 == 0, ld % 8 == 0, pointers 16-byte aligned; y must not overlap the
+ * inputs. */
+w8a8_status w8a8_swiglu(const uint16_t* gate, const uint16_t* up, int64_t ld, uint16_t* y,
+                        int64_t M, int64_t N, hipStream_t stream);
+
 /* ---- whole paths: quantize x into the workspace, then GEMM + epilogue --------
  * `workspace` must hold w8a8_workspace_bytes(M, K) bytes (256-byte aligned is
  * best; 16-byte aligned is required) and is used as scratch for the quantized

@@ -24,6 +24,9 @@ What each call follows (pages on quantized Clef checkpoints):
   scale + bias (+ paired gate/up SwiGLU) epilogue (INT8 ConvRot card,
   Benefits list; "Loading CLEF INT8", fuse_mlp and packed gate/up).
 * ``linear`` / ``gateup_swiglu`` / ``fp8_linear`` -- the whole path.
+* ``swiglu_bf16`` / ``gateup_unfused`` -- the unfused gate/up path
+  ("Loading CLEF INT8", fuse_mlp=False): SwiGLU applied to the separately
+  rounded bf16 gate and up projections.
 
 No function here carries a "parity unpinned" mark: each is pinned by the
 ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``.
@@ -92,6 +95,8 @@ def _load():
         "orc_linear": (None, [P, P, P, P, P, I64, I64, I64, I, I]),
         "orc_gateup_swiglu": (None, [P, P, P, P, P, I64, I64, I64, I, I]),
         "orc_fp8_linear": (None, [P, P, P, P, P, I64, I64, I64, I, I]),
+        "orc_swiglu_bf16": (None, [P, P, I64, P, I64, I64, I]),
+        "orc_gateup_unfused": (None, [P, P, P, P, P, I64, I64, I64, I, I]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -285,3 +290,21 @@ def gateup_swiglu(x, w_gateup, s_ch, bias=None, rot_block=0, threads=None):
 
 def fp8_linear(x, w, s_ch, bias=None, rot_block=0, threads=None):
     return _path_call("orc_fp8_linear", x, w, s_ch, bias, rot_block, w.shape[0], np.uint8, threads)
+
+
+def swiglu_bf16(g, u, threads=None):
+    """bf16 bits of silu(g) * u for bf16 bit arrays g, u [M, N] (one rounding)."""
+    lib = _load()
+    g = np.ascontiguousarray(g, dtype=np.uint16)
+    u = np.ascontiguousarray(u, dtype=np.uint16)
+    assert g.shape == u.shape and g.ndim == 2
+    M, N = g.shape
+    y = np.empty((M, N), dtype=np.uint16)
+    lib.orc_swiglu_bf16(_ptr(g), _ptr(u), N, _ptr(y), M, N, threads or default_threads())
+    return y
+
+
+def gateup_unfused(x, w_gateup, s_ch, bias=None, rot_block=0, threads=None):
+    """Unfused gate/up: linear onto the 2N packed rows (bf16), then swiglu_bf16 of its halves."""
+    return _path_call("orc_gateup_unfused", x, w_gateup, s_ch, bias, rot_block,
+                      w_gateup.shape[0] // 2, np.int8, threads)

@@ -433,6 +433,32 @@ void orc_gateup_swiglu(const uint16_t* x, const int8_t* w, const float* s_ch, co
   orc_gemm_swiglu(q.data(), s.data(), w, s_ch, bias, y, M, N, K, nthreads);
 }
 
+// ---- unfused gate/up ("Loading CLEF INT8": fuse_mlp=False) ----
+// The gate and up projections are separate linears whose bf16 outputs are then
+// combined: y = bf16(silu(g) * u) with g, u the bf16 values (already rounded).
+// g and u are [M, N] with rows ld elements apart; y is dense [M, N].
+void orc_swiglu_bf16(const uint16_t* g, const uint16_t* u, int64_t ld, uint16_t* y, int64_t M,
+                     int64_t N, int nthreads) {
+  parallel_for(M * N, nthreads, [&](int64_t lo, int64_t hi) {
+    for (int64_t e = lo; e < hi; ++e) {
+      int64_t m = e / N, n = e % N;
+      double gv = (double)bf16_to_f32(g[m * ld + n]);
+      double uv = (double)bf16_to_f32(u[m * ld + n]);
+      y[e] = f64_to_bf16(silu_times(gv, uv));
+    }
+  });
+}
+
+// The unfused path: quantize x once (both linears see the same activations),
+// project onto all 2N packed rows with the dequant epilogue (bf16 [M, 2N]:
+// gate columns 0..N-1, up columns N..2N-1), then SwiGLU on the rounded values.
+void orc_gateup_unfused(const uint16_t* x, const int8_t* w, const float* s_ch, const uint16_t* bias,
+                        uint16_t* y, int64_t M, int64_t N, int64_t K, int rot_block, int nthreads) {
+  std::vector<uint16_t> h((size_t)(M * 2 * N));
+  orc_linear(x, w, s_ch, bias, h.data(), M, 2 * N, K, rot_block, nthreads);
+  orc_swiglu_bf16(h.data(), h.data() + N, 2 * N, y, M, N, nthreads);
+}
+
 void orc_fp8_linear(const uint16_t* x, const uint8_t* w, const float* s_ch, const uint16_t* bias,
                     uint16_t* y, int64_t M, int64_t N, int64_t K, int rot_block, int nthreads) {
   std::vector<uint8_t> q((size_t)(M * K));

@@ -46,6 +46,7 @@ def lib():
         "w8a8_gemm_dequant_packed": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
         "w8a8_gemm_swiglu_packed": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
         "w8a8_fp8_gemm_dequant_packed": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
+        "w8a8_swiglu": (I, [P, P, I64, P, I64, I64, P]),
         "w8a8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_gateup_swiglu_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_fp8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
@@ -69,7 +70,7 @@ def test_header_declares_the_documented_entry_points():
             "w8a8_packed_bytes", "w8a8_pack_weight", "w8a8_linear_packed",
             "w8a8_gateup_swiglu_packed", "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed",
             "w8a8_quantize_act_fp8_packed", "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed",
-            "w8a8_fp8_gemm_dequant_packed"}
+            "w8a8_fp8_gemm_dequant_packed", "w8a8_swiglu"}
     assert want <= set(declared_symbols())
 
 
@@ -163,6 +164,19 @@ def test_whole_path_argument_checks(lib):
         assert g(A, A, A, None, A, 4, 8, 256, 0, A, ws - 1, None) == BADARG
         assert g(A, A, A, None, A, 4, 12, 256, 0, A, ws, None) == SHAPE
         assert g(None, None, None, None, None, 0, 8, 256, 0, None, 0, None) == OK
+
+
+def test_swiglu_argument_checks(lib):
+    f = lib.w8a8_swiglu
+    assert f(None, A, 16, A, 4, 16, None) == NULLP
+    assert f(A, A, 16, None, 4, 16, None) == NULLP
+    assert f(A, A, 16, A, 4, 12, None) == SHAPE        # N % 8
+    assert f(A, A, 8, A, 4, 16, None) == SHAPE         # ld < N
+    assert f(A, A, 20, A, 4, 16, None) == SHAPE        # ld % 8
+    assert f(A, A, 16, A, -1, 16, None) == SHAPE
+    assert f(U, A, 16, A, 4, 16, None) == MISALIGNED
+    assert f(A, U, 16, A, 4, 16, None) == MISALIGNED
+    assert f(None, None, 32, None, 0, 16, None) == OK  # M == 0
 
 
 def test_pack_weight_argument_checks(lib):

@@ -181,3 +181,61 @@ def test_linear_error_bound_against_unquantized(orc):
     # and the error is a small fraction of the output scale (the method is usable)
     rel = np.linalg.norm(y - exact) / np.linalg.norm(exact)
     assert rel < 0.05
+
+
+# ---- unfused gate/up ("Loading CLEF INT8", fuse_mlp=False) ----------------------
+def _bf16_bits_of(v):
+    return W.bits(torch.tensor(v, dtype=torch.float64).to(torch.bfloat16))
+
+
+def test_swiglu_bf16_against_expit(orc):
+    """silu(g) * u on bf16 inputs, one rounding: within half a bf16 ulp of an fp64
+    evaluation through scipy's logistic function (an implementation independent of
+    the oracle's), over a wide range of magnitudes and signs."""
+    g_t = torch.randn(64, 96, generator=torch.Generator().manual_seed(61), dtype=torch.float64) * 4
+    u_t = torch.randn(64, 96, generator=torch.Generator().manual_seed(62), dtype=torch.float64) * 3
+    g_t[0, :8] = torch.tensor([0.0, -0.0, 1e-30, -1e-30, 80.0, -80.0, 1000.0, -1000.0])
+    g, u = W.bits(g_t.to(torch.bfloat16)), W.bits(u_t.to(torch.bfloat16))
+    y = orc.swiglu_bf16(g, u)
+    gv, uv = _bf16_to_f64(g), _bf16_to_f64(u)
+    ref = gv * expit(gv) * uv
+    got = _bf16_to_f64(y)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 1e-38))) - 7)
+    assert np.all(np.abs(got - ref) <= 0.5 * ulp * (1 + 1e-9))
+
+
+def test_swiglu_bf16_identities(orc):
+    """silu(g) - silu(-g) = g (with u = 1, up to the two output roundings); silu(0) = 0;
+    silu(g) -> g for large g and -> -0 for large negative g; odd in u."""
+    g = _bf16_bits_of(np.linspace(-12, 12, 97).reshape(1, -1))
+    gn = _bf16_bits_of(-np.linspace(-12, 12, 97).reshape(1, -1))
+    one = _bf16_bits_of(np.ones((1, 97)))
+    y_pos, y_neg = _bf16_to_f64(orc.swiglu_bf16(g, one)), _bf16_to_f64(orc.swiglu_bf16(gn, one))
+    gv = _bf16_to_f64(g)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(gv), 1e-38))) - 7)
+    assert np.all(np.abs((y_pos - y_neg) - gv) <= ulp)
+    assert _bf16_to_f64(orc.swiglu_bf16(_bf16_bits_of([[0.0]]), _bf16_bits_of([[5.0]])))[0, 0] == 0.0
+    big = orc.swiglu_bf16(_bf16_bits_of([[64.0, -800.0]]), _bf16_bits_of([[3.0, 3.0]]))
+    assert _bf16_to_f64(big)[0, 0] == 192.0
+    assert _bf16_to_f64(big)[0, 1] == 0.0 and np.signbit(_bf16_to_f64(big)[0, 1])
+    mu = orc.swiglu_bf16(g, _bf16_bits_of(-np.ones((1, 97))))
+    assert np.array_equal(_bf16_to_f64(mu), -y_pos)
+
+
+def test_gateup_unfused_is_linear_then_swiglu(orc):
+    """The unfused path rounds gate and up to bf16 (the 2N-column linear) before the
+    SwiGLU, so it equals swiglu_bf16 of the linear's halves -- and differs from the
+    fused epilogue only by that intermediate rounding."""
+    wl = W.custom("gateup", 33, 384, 40, 128, bias=True, seed=63)
+    inp = W.make_inputs(wl)
+    x, w, bias = W.bits(inp.x), W.bits(inp.w), W.bits(inp.bias)
+    wq, s_ch = orc.quantize_i8(w, 128)
+    h = orc.linear(x, wq, s_ch, bias, 128)
+    assert h.shape == (33, 80)
+    y = orc.gateup_unfused(x, wq, s_ch, bias, 128)
+    assert np.array_equal(y, orc.swiglu_bf16(h[:, :40], h[:, 40:]))
+    fused = _bf16_to_f64(orc.gateup_swiglu(x, wq, s_ch, bias, 128))
+    unf = _bf16_to_f64(y)
+    scale = np.sqrt(np.mean(fused ** 2))
+    assert np.max(np.abs(unf - fused)) <= 0.03 * scale          # one extra bf16 rounding of g and u
+    assert not np.array_equal(unf, fused)

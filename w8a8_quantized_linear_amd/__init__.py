@@ -28,6 +28,7 @@ __all__ = [
     "w8a8_gateup_swiglu", "w8a8_fp8_linear", "w8a8_linear_packed", "w8a8_gateup_swiglu_packed",
     "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed", "w8a8_quantize_act_fp8_packed",
     "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed", "w8a8_fp8_gemm_dequant_packed",
+    "w8a8_swiglu",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
@@ -57,6 +58,7 @@ _SIGS = {
     "w8a8_gemm_dequant_packed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_fp8_gemm_dequant_packed": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_swiglu": (_I, [_P, _P, _I64, _P, _I64, _I64, _P]),
     "w8a8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_gateup_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_fp8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
@@ -260,6 +262,24 @@ def w8a8_fp8_gemm_dequant_packed(q_packed, s_tok, w_packed, s_ch, K, bias=None, 
     """w8a8_fp8_gemm_dequant on packed operands; M = len(s_tok), N = len(s_ch)."""
     return _epi_packed("w8a8_fp8_gemm_dequant_packed", q_packed, s_tok, w_packed, s_ch, bias,
                        s_tok.shape[0], s_ch.shape[0], K, torch.uint8, out)
+
+
+# ------------------------------------------------- unfused gate/up SwiGLU ----
+def w8a8_swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor] = None):
+    """y bf16 [M, N] = silu(gate) * up for bf16 [M, N] views with the same row stride
+    (e.g. the two halves of a [M, 2N] projection: h[:, :N], h[:, N:])."""
+    for t, name in ((gate, "gate"), (up, "up")):
+        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_cuda:
+            raise ValueError(f"{name}: expected a 2-D bf16 device tensor")
+        if t.stride(1) != 1:
+            raise ValueError(f"{name}: rows must be contiguous")
+    if gate.shape != up.shape or gate.stride(0) != up.stride(0):
+        raise ValueError("gate and up must have the same shape and row stride")
+    M, N = gate.shape
+    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=gate.device)
+    _check(_lib.w8a8_swiglu(_ptr(gate), _ptr(up), gate.stride(0), _ptr(y), M, N, _stream()),
+           "w8a8_swiglu")
+    return y
 
 
 # ------------------------------------------------------------ whole paths ----

@@ -142,6 +142,19 @@ w8a8_status w8a8_pack_weight(const void* w, int64_t rows, int64_t K, void* w_pac
   return launched(w8a8::launch_pack_rows(w, rows, K, w_packed, stream));
 }
 
+w8a8_status w8a8_swiglu(const uint16_t* gate, const uint16_t* up, int64_t ld, uint16_t* y, int64_t M,
+                        int64_t N, hipStream_t stream) {
+  if (M < 0 || N < 8 || N % 8 != 0 || ld < N || ld % 8 != 0 || M > (int64_t)1 << 31 ||
+      N > (int64_t)1 << 30)
+    return W8A8_ERR_BAD_SHAPE;
+  if (M == 0) return W8A8_OK;
+  if (!gate || !up || !y) return W8A8_ERR_NULL_POINTER;
+  if (!aligned16(gate) || !aligned16(up) || !aligned16(y)) return W8A8_ERR_MISALIGNED;
+  w8a8_status st;
+  if ((st = check_device()) != W8A8_OK) return st;
+  return launched(w8a8::launch_swiglu(gate, up, ld, y, M, N, stream));
+}
+
 w8a8_status w8a8_quantize_act(const uint16_t* x, int64_t M, int64_t K, int rot_block, int8_t* q,
                               float* s_tok, hipStream_t stream) {
   return quantize(x, M, K, rot_block, false, false, q, s_tok, stream);

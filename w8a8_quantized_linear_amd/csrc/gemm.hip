@@ -100,6 +100,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// silu(g) = g * sigmoid(g), sigmoid(g) = (g >= 0 ? 1 : e) / (1 + e) with
+// e = exp(-|g|): no overflow, and very negative g gives its tiny value, not 0.
+__device__ __forceinline__ float silu_f32(float g) {
+  const float e = expf(-fabsf(g));
+  return g * ((g >= 0.0f ? 1.0f : e) / (1.0f + e));
+}
+
 __device__ __forceinline__ void bf16x4(uint2 b, float* f) {
   f[0] = __uint_as_float(b.x << 16);
   f[1] = __uint_as_float(b.x & 0xffff0000u);
@@ -203,7 +210,7 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[TN][TM], const float
             for (int v = 0; v < 4; ++v) {
               const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
               const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
-              o[v] = f32_to_bf16_rne(g / (1.0f + __expf(-g)) * u);
+              o[v] = f32_to_bf16_rne(silu_f32(g) * u);
             }
             *reinterpret_cast<uint2*>(yrow + n0) =
                 make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));

@@ -25,6 +25,11 @@ hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const vo
                        const float* s_tok, const void* b, const float* s_ch, const uint16_t* bias,
                        void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
+// y [M, N] (dense) = bf16(silu(g) * u), g and u bf16 [M, N] with rows ld elements
+// apart (N % 8 == 0, ld % 8 == 0).
+hipError_t launch_swiglu(const uint16_t* g, const uint16_t* u, int64_t ld, uint16_t* y, int64_t M,
+                         int64_t N, hipStream_t stream);
+
 // Row-major codes [rows, K] -> packed layout (K % 64 == 0; padding rows zero).
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream);
 
