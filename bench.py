@@ -51,10 +51,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("fused", "unfused"), default="fused",
-                    help="gate/up workloads: paired SwiGLU epilogue (fused) or the fuse_mlp=False "
-                         "chain -- GEMM onto the 2N packed rows with the dequant epilogue, then "
-                         "w8a8_swiglu (unfused)")
+    ap.add_argument("--path", choices=("fused", "unfused", "single"), default="fused",
+                    help="fused: quantizer and GEMM with its fused epilogue, timed per kernel; "
+                         "unfused (gate/up workloads): the fuse_mlp=False chain -- GEMM onto the 2N "
+                         "packed rows with the dequant epilogue, then w8a8_swiglu; single (int8): "
+                         "the whole-path entry point as one call (one kernel for short batches)")
     ap.add_argument("--drift", action="store_true",
                     help="instead of timing: relative L2 drift of every workload's W8A8 output from "
                          "the fp64 unquantized projection, without and with the block rotation")
@@ -200,8 +201,12 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
     unfused = args.path == "unfused"
+    single = args.path == "single"
     if unfused and wl.kind != "gateup":
         print("bench.py: --path unfused applies to gate/up workloads only", file=sys.stderr)
+        sys.exit(2)
+    if single and wl.kind == "fp8":
+        print("bench.py: --path single applies to int8 workloads only", file=sys.stderr)
         sys.exit(2)
     inp = W.make_inputs(wl)
     fp8 = wl.kind == "fp8"
@@ -246,9 +251,25 @@ def main():
         gargs = [(qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(),
                   M, n_out, K, stream) for i in range(copies)]
     n_ev = 4 if unfused else 3
+    if single:
+        n_ev = 2
+        wsz = lib.workspace_bytes(M, K)
+        wss = [torch.empty((wsz,), dtype=torch.uint8, device=dev) for _ in range(copies)]
+        pfn = L.w8a8_linear_packed if wl.kind == "linear" else L.w8a8_gateup_swiglu_packed
+        pargs = [(xs[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(), M, n_out, K,
+                  wl.rot_block, wss[i].data_ptr(), wsz, stream) for i in range(copies)]
 
     def step(i, evs=None):
         c = i % copies
+        if single:
+            if evs is not None:
+                evs[0].record()
+            st = pfn(*pargs[c])
+            if evs is not None:
+                evs[1].record()
+            if st:
+                raise RuntimeError(f"library call failed with status {st}")
+            return
         if evs is not None:
             evs[0].record()
         st = qfn(*qargs[c])
@@ -287,7 +308,8 @@ def main():
     torch.cuda.synchronize()
 
     tq = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3   # s per quantizer launch
-    tg = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3   # s per GEMM launch
+    tg = (sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3   # s per GEMM launch
+          if not single else tq)
     ms_per_step = wall / args.steps * 1e3
     ops = 2 * M * Nw * K
     q_bytes = 2 * M * K + M * K + 4 * M                      # read bf16 x, write codes + scales
@@ -310,7 +332,8 @@ def main():
         "dtype": "fp8-e4m3" if fp8 else "i8",
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": wl.name, "M": M, "K": K, "N": n_out, "weight_rows": Nw,
-                   "rot_block": wl.rot_block, "path": wl.kind + ("-unfused" if unfused else ""),
+                   "rot_block": wl.rot_block,
+                   "path": wl.kind + ("-unfused" if unfused else "") + ("-single-call" if single else ""),
                    "parallelism": "single GPU",
                    "operand_copies": copies},
         "pct_of_peak": 100.0 * ops / (ms_per_step * 1e-3) / (peak * 1e12),
@@ -322,6 +345,11 @@ def main():
                       "frac": q_bytes / tq / 1e9 / PEAK_HBM_GBS, "avg_launch_us": tq * 1e6,
                       "algorithmic_bytes": q_bytes},
     }
+    if single:
+        del out["quantizer"]
+        out["roofline"]["kernel"] = ("whole-path call: one kernel (quantizer + GEMM + epilogue) for "
+                                     "short batches, else the quantizer and the GEMM")
+        out["roofline"]["algorithmic_bytes"] = q_bytes + g_bytes - M * K - 4 * M   # codes not re-read
     if unfused:
         tsw = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
         sw_bytes = 6 * M * n_out                             # read gate + up, write y (bf16)

@@ -191,9 +191,13 @@ w8a8_status w8a8_swiglu(const uint16_t* gate, const uint16_t* up, int64_t ld, ui
  * `workspace` must hold w8a8_workspace_bytes(M, K) bytes (256-byte aligned is
  * best; 16-byte aligned is required) and is used as scratch for the quantized
  * activations and their scales; its contents afterwards are those codes (in
- * the packed layout) and scales.  Two kernels are enqueued on `stream`.  The
- * plain forms take the row-major weight; the *_packed forms take the weight
- * as written by w8a8_pack_weight (same arithmetic, same results). */
+ * the packed layout) and scales.  Two kernels are enqueued on `stream` (the
+ * quantizer, then the GEMM) -- or, for short int8 batches (M <= 512,
+ * K <= 1024, at most 256 tiles of 32 tokens x 64 weight rows), one kernel
+ * that quantizes each tile's rows itself, with the same codes, scales and
+ * outputs.  The plain forms take the
+ * row-major weight; the *_packed forms take the weight as written by
+ * w8a8_pack_weight (same arithmetic, same results). */
 w8a8_status w8a8_linear(const uint16_t* x, const int8_t* w, const float* s_ch, const uint16_t* bias,
                         uint16_t* y, int64_t M, int64_t N, int64_t K, int rot_block,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);

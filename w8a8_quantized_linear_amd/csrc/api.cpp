@@ -97,6 +97,10 @@ w8a8_status whole_path(w8a8::Epi epi, bool fp8, bool w_packed, const uint16_t* x
   if ((st = check_device()) != W8A8_OK) return st;
   uint8_t* q = static_cast<uint8_t*>(workspace);
   float* s_tok = reinterpret_cast<float*>(q + align256(w8a8_packed_bytes(M, K)));
+  // short batches: one kernel quantizes inside the GEMM (same codes, scales and outputs)
+  if (!fp8 && w8a8::short_path_fits(M, N, K, epi))
+    return launched(w8a8::launch_linear_short(epi, x, w, w_packed, s_ch, bias, y, M, N, K, rot_block, q,
+                                              s_tok, stream));
   st = launched(w8a8::launch_quantize(x, M, K, rot_block, fp8, /*packed=*/true, q, s_tok, stream));
   if (st != W8A8_OK) return st;
   return launched(w8a8::launch_gemm(epi, fp8, /*packed_a=*/true, w_packed, q, s_tok, w, s_ch, bias, y,

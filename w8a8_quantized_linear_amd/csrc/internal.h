@@ -30,6 +30,18 @@ hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const vo
 hipError_t launch_swiglu(const uint16_t* g, const uint16_t* u, int64_t ld, uint16_t* y, int64_t M,
                          int64_t N, hipStream_t stream);
 
+// Single-launch short-input whole path (int8 dequant or SwiGLU): quantizes x
+// inside the GEMM kernel; writes the packed codes and the scales to q_ws / s_ws
+// like the two-kernel path.  Used when short_path_fits().
+constexpr int64_t kShortMaxK = 1024;
+constexpr int64_t kShortMaxM = 512;
+constexpr int64_t kShortMaxTiles = 256;   // tiles of 32 tokens x 64 weight rows
+bool short_path_fits(int64_t M, int64_t N, int64_t K, Epi epi);
+hipError_t launch_linear_short(Epi epi, const uint16_t* x, const void* w, bool w_packed,
+                               const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
+                               int64_t N, int64_t K, int rot_block, void* q_ws, float* s_ws,
+                               hipStream_t stream);
+
 // Row-major codes [rows, K] -> packed layout (K % 64 == 0; padding rows zero).
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream);
 

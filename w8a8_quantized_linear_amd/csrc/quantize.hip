@@ -34,11 +34,13 @@
 //     instruction into one contiguous span.  Neither straddles a 64-byte group,
 //     so the packed form only changes the address.
 #include "internal.h"
+#include "quant_math.h"
 
 namespace w8a8 {
 namespace {
 
-constexpr int kEPL = 32;  // bf16 elements per lane per chunk
+using namespace qm;
+
 constexpr int kXcds = 8;
 
 // Block id -> the block's place in row order.  The hardware deals consecutive
@@ -49,47 +51,6 @@ __device__ __forceinline__ int64_t row_block_of(int bid, int nblocks) {
   const int q = nblocks / kXcds, r = nblocks % kXcds;
   const int xcd = bid % kXcds, idx = bid / kXcds;
   return (xcd < r) ? (int64_t)xcd * (q + 1) + idx : (int64_t)r * (q + 1) + (int64_t)(xcd - r) * q + idx;
-}
-
-// fl64(2^-3.5) = fl64(sqrt(2)/2) / 8
-constexpr double kInvSqrt128 = 0x1.6a09e667f3bcdp-4;
-
-__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
-__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-
-// fp64 value of the lane whose quad position differs in the bits of MASK (1 or 2).
-template <int MASK>
-__device__ __forceinline__ double quad_xor(double v) {
-  // quad_perm selectors: lane i of each quad reads lane i ^ MASK
-  constexpr int ctrl = MASK == 1 ? 0xB1 : 0x4E;  // [1,0,3,2] / [2,3,0,1]
-  const long long bits = __double_as_longlong(v);
-  const int lo = __builtin_amdgcn_mov_dpp((int)bits, ctrl, 0xF, 0xF, false);
-  const int hi = __builtin_amdgcn_mov_dpp((int)(bits >> 32), ctrl, 0xF, 0xF, false);
-  return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
-}
-
-__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
-  uint32_t ia = (uint32_t)(int)a & 0xffu, ib = (uint32_t)(int)b & 0xffu;
-  uint32_t ic = (uint32_t)(int)c & 0xffu, id = (uint32_t)(int)d & 0xffu;
-  return ia | (ib << 8) | (ic << 16) | (id << 24);
-}
-
-// Code of fl32(y / s) rounded half to even, via the reciprocal r = fl32(1/s).
-__device__ __forceinline__ float int8_code(float y, float s, float r) {
-  const float t = y * r;
-  const float k = __builtin_rintf(t);
-  // |t - y/s| <= 2^-16 and |fl32(y/s) - y/s| <= 2^-18 for |y/s| < 128: only a t
-  // within 2^-15 of a half-integer can round differently from the IEEE
-  // quotient.  (Written so that a non-finite t, from a subnormal s, also takes
-  // the exact path.)
-  if (__builtin_expect(!(fabsf(fabsf(t - k) - 0.5f) >= 0x1p-14f), 0)) return __builtin_rintf(y / s);
-  return k;
 }
 
 // T threads per row (a multiple of 64), CMAX chunks of 32 elements per lane.
@@ -135,39 +96,7 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
 #pragma unroll
   for (int i = 0; i < CMAX; ++i) {
     if constexpr (ROT) {
-      double v[kEPL];
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t w = raw[i][j / 4][j % 4];
-        v[2 * j] = (double)bf16lo(w);
-        v[2 * j + 1] = (double)bf16hi(w);
-      }
-      // element index bits 0..4 live in the lane
-#pragma unroll
-      for (int h = 1; h < kEPL; h <<= 1) {
-#pragma unroll
-        for (int j = 0; j < kEPL; ++j) {
-          if (!(j & h)) {
-            const double a = v[j], b = v[j | h];
-            v[j] = a + b;
-            v[j | h] = a - b;
-          }
-        }
-      }
-      // element index bits 5, 6 are the lane's position in its quad
-      {
-        const double sgn = (lane & 1) ? -1.0 : 1.0;
-#pragma unroll
-        for (int j = 0; j < kEPL; ++j) v[j] = __builtin_fma(sgn, v[j], quad_xor<1>(v[j]));
-      }
-      {
-        const double sgn = (lane & 2) ? -1.0 : 1.0;
-#pragma unroll
-        for (int j = 0; j < kEPL; ++j) v[j] = __builtin_fma(sgn, v[j], quad_xor<2>(v[j]));
-      }
-      // (lower lane: v + p; upper lane: p - v; both exact)
-#pragma unroll
-      for (int j = 0; j < kEPL; ++j) y[i][j] = (float)(v[j] * kInvSqrt128);
+      rotate_chunk(raw[i], lane, y[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
