@@ -18,6 +18,12 @@ steps then run again with HIP events bracketing each kernel on the launch
 stream, which gives the per-kernel average durations (event records idle the
 GPU between kernels, so they stay out of the throughput figure).
 
+Other paths (--path): the unfused gate/up chain, the whole-path call as one
+library call, and for gate/up workloads the SwiGLU output quantized for the next
+linear either inside the GEMM epilogue (swiglu-quant: block codes, then the
+rescaling pass) or by the per-token quantizer after the bf16 output
+(swiglu-then-quant); the ops counted stay those of the GEMM.
+
 Prints one JSON line: metric = TOPS of the whole path (2*M*N_w*K ops per step
 over the step time), the roofline of the dominant kernel (the GEMM) with its
 event-timed average duration, the quantizer's bandwidth, and the CPU oracle
@@ -51,11 +57,19 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("fused", "unfused", "single"), default="fused",
+    ap.add_argument("--path", choices=("fused", "unfused", "single", "swiglu-quant", "swiglu-then-quant"),
+                    default="fused",
                     help="fused: quantizer and GEMM with its fused epilogue, timed per kernel; "
                          "unfused (gate/up workloads): the fuse_mlp=False chain -- GEMM onto the 2N "
                          "packed rows with the dequant epilogue, then w8a8_swiglu; single (int8): "
-                         "the whole-path entry point as one call (one kernel for short batches)")
+                         "the whole-path entry point as one call (one kernel for short batches); "
+                         "swiglu-quant (gate/up): the SwiGLU output quantized for the next linear "
+                         "inside the GEMM epilogue (block codes), then the rescaling pass; "
+                         "swiglu-then-quant (gate/up): the same codes' reference route -- fused "
+                         "SwiGLU GEMM writing bf16, then the per-token quantizer on it")
+    ap.add_argument("--rot-out", type=int, choices=(0, 128), default=128,
+                    help="rotation block of the next linear's input for the swiglu-quant paths "
+                         "(the down projection rotates by 128)")
     ap.add_argument("--drift", action="store_true",
                     help="instead of timing: relative L2 drift of every workload's W8A8 output from "
                          "the fp64 unquantized projection, without and with the block rotation")
@@ -131,7 +145,7 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> dict:
     return rec
 
 
-def cpu_baseline(wl, inp, unfused=False):
+def cpu_baseline(wl, inp, unfused=False, rot_out=None):
     """The CPU oracle, as it stands, on the whole workload (all rows), on this host."""
     import numpy as np
     import oracle
@@ -147,7 +161,10 @@ def cpu_baseline(wl, inp, unfused=False):
     fn = {"linear": oracle.linear, "gateup": oracle.gateup_unfused if unfused else oracle.gateup_swiglu,
           "fp8": oracle.fp8_linear}[wl.kind]
     t0 = time.perf_counter()
-    fn(xs, wq, s_ch, bias, wl.rot_block, threads)
+    if rot_out is not None:   # gate/up SwiGLU whose output is quantized for the next linear
+        oracle.gateup_swiglu_quant(xs, wq, s_ch, bias, wl.rot_block, rot_out, threads)
+    else:
+        fn(xs, wq, s_ch, bias, wl.rot_block, threads)
     dt = time.perf_counter() - t0
     ops = 2 * rows * wl.n_w * wl.K
     return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
@@ -202,8 +219,10 @@ def main():
     del calib_src, calib_dst
     unfused = args.path == "unfused"
     single = args.path == "single"
-    if unfused and wl.kind != "gateup":
-        print("bench.py: --path unfused applies to gate/up workloads only", file=sys.stderr)
+    quantout = args.path == "swiglu-quant"
+    then_quant = args.path == "swiglu-then-quant"
+    if (unfused or quantout or then_quant) and wl.kind != "gateup":
+        print(f"bench.py: --path {args.path} applies to gate/up workloads only", file=sys.stderr)
         sys.exit(2)
     if single and wl.kind == "fp8":
         print("bench.py: --path single applies to int8 workloads only", file=sys.stderr)
@@ -230,6 +249,12 @@ def main():
     ys = [torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     # unfused: the bf16 gate/up projection [M, 2N] between the GEMM and the SwiGLU pass
     hs = [torch.empty((M, Nw), dtype=torch.bfloat16, device=dev) for _ in range(copies)] if unfused else []
+    # swiglu-quant paths: the next linear's input codes (packed) + scales, and the block amax
+    nblk = (n_out + 127) // 128
+    if quantout or then_quant:
+        cs = [torch.empty((lib.packed_bytes(M, n_out),), dtype=torch.int8, device=dev) for _ in range(copies)]
+        s2 = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(copies)]
+        am = [torch.empty((M, nblk), dtype=torch.float32, device=dev) for _ in range(copies)] if quantout else []
     torch.cuda.synchronize()
 
     L = lib._lib
@@ -250,38 +275,40 @@ def main():
     else:
         gargs = [(qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(),
                   M, n_out, K, stream) for i in range(copies)]
-    n_ev = 4 if unfused else 3
+    # calls[c]: the library calls of one step on operand copy c, in order
+    calls = [[(qfn, qargs[i]), (gfn, gargs[i])] for i in range(copies)]
+    if unfused:
+        for i in range(copies):
+            calls[i].append((L.w8a8_swiglu, sargs[i]))
     if single:
-        n_ev = 2
         wsz = lib.workspace_bytes(M, K)
         wss = [torch.empty((wsz,), dtype=torch.uint8, device=dev) for _ in range(copies)]
         pfn = L.w8a8_linear_packed if wl.kind == "linear" else L.w8a8_gateup_swiglu_packed
-        pargs = [(xs[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(), M, n_out, K,
-                  wl.rot_block, wss[i].data_ptr(), wsz, stream) for i in range(copies)]
+        calls = [[(pfn, (xs[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(), M, n_out, K,
+                         wl.rot_block, wss[i].data_ptr(), wsz, stream))] for i in range(copies)]
+    if quantout:
+        calls = [[(qfn, qargs[i]),
+                  (L.w8a8_gemm_swiglu_blockquant_packed,
+                   (qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, M, n_out, K,
+                    args.rot_out, cs[i].data_ptr(), am[i].data_ptr(), None, stream)),
+                  (L.w8a8_requantize_blocks_packed,
+                   (cs[i].data_ptr(), am[i].data_ptr(), M, n_out, s2[i].data_ptr(), stream))]
+                 for i in range(copies)]
+    if then_quant:
+        for i in range(copies):
+            calls[i].append((L.w8a8_quantize_act_packed,
+                             (ys[i].data_ptr(), M, n_out, args.rot_out, cs[i].data_ptr(), s2[i].data_ptr(),
+                              stream)))
+    n_ev = len(calls[0]) + 1
 
     def step(i, evs=None):
-        c = i % copies
-        if single:
+        st = 0
+        for j, (fn, a) in enumerate(calls[i % copies]):
             if evs is not None:
-                evs[0].record()
-            st = pfn(*pargs[c])
-            if evs is not None:
-                evs[1].record()
-            if st:
-                raise RuntimeError(f"library call failed with status {st}")
-            return
+                evs[j].record()
+            st |= fn(*a)
         if evs is not None:
-            evs[0].record()
-        st = qfn(*qargs[c])
-        if evs is not None:
-            evs[1].record()
-        st |= gfn(*gargs[c])
-        if evs is not None:
-            evs[2].record()
-        if unfused:
-            st |= L.w8a8_swiglu(*sargs[c])
-            if evs is not None:
-                evs[3].record()
+            evs[-1].record()
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -307,16 +334,18 @@ def main():
         step(i, evs[i])
     torch.cuda.synchronize()
 
-    tq = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps * 1e-3   # s per quantizer launch
-    tg = (sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps * 1e-3   # s per GEMM launch
-          if not single else tq)
+    def avg(j):  # s per launch of call j
+        return sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps * 1e-3
+    tq = avg(0)                       # quantizer (or the single whole-path call)
+    tg = avg(1) if not single else tq  # GEMM
     ms_per_step = wall / args.steps * 1e3
     ops = 2 * M * Nw * K
     q_bytes = 2 * M * K + M * K + 4 * M                      # read bf16 x, write codes + scales
     out_cols = Nw if unfused else n_out                      # the unfused GEMM writes [M, 2N]
-    g_bytes = M * K + Nw * K + 4 * (M + Nw) + M * out_cols * 2 + (0 if bias0 is None else 2 * Nw)
+    out_bytes = M * n_out + 4 * M * nblk if quantout else M * out_cols * 2   # block codes + amax, or bf16
+    g_bytes = M * K + Nw * K + 4 * (M + Nw) + out_bytes + (0 if bias0 is None else 2 * Nw)
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
-    traffic = stored_traffic(wl.name + ("-unfused" if unfused else ""))
+    traffic = stored_traffic(wl.name + ("-unfused" if unfused else "") + ("-swiglu-quant" if quantout else ""))
 
     out = {
         "metric": "W8A8 linear TOPS incl. quant+dequant, % int8 MFMA peak; quantizer GB/s",
@@ -333,7 +362,8 @@ def main():
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": {"workload": wl.name, "M": M, "K": K, "N": n_out, "weight_rows": Nw,
                    "rot_block": wl.rot_block,
-                   "path": wl.kind + ("-unfused" if unfused else "") + ("-single-call" if single else ""),
+                   "path": wl.kind + ("-unfused" if unfused else "") + ("-single-call" if single else "")
+                   + (f"-{args.path}-rot{args.rot_out}" if quantout or then_quant else ""),
                    "parallelism": "single GPU",
                    "operand_copies": copies},
         "pct_of_peak": 100.0 * ops / (ms_per_step * 1e-3) / (peak * 1e12),
@@ -357,8 +387,23 @@ def main():
                          "unit": "GB/s", "frac": sw_bytes / tsw / 1e9 / PEAK_HBM_GBS,
                          "avg_launch_us": tsw * 1e6, "algorithmic_bytes": sw_bytes}
         out["roofline"]["kernel"] = "gemm_tile (GEMM + dequant epilogue onto 2N columns)"
+    if quantout:
+        trq = avg(2)
+        rq_bytes = 2 * M * n_out + 4 * M * nblk + 4 * M           # codes read + written, amax, scales
+        out["requantize"] = {"bound": "hbm", "achieved": rq_bytes / trq / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": rq_bytes / trq / 1e9 / PEAK_HBM_GBS,
+                             "avg_launch_us": trq * 1e6, "algorithmic_bytes": rq_bytes}
+        out["roofline"]["kernel"] = ("gemm_tile (GEMM + SwiGLU epilogue quantizing 128-column blocks "
+                                     "for the next linear)")
+    if then_quant:
+        th = avg(2)
+        qh_bytes = 2 * M * n_out + M * n_out + 4 * M
+        out["quantizer_h"] = {"bound": "hbm", "achieved": qh_bytes / th / 1e9, "peak": PEAK_HBM_GBS,
+                              "unit": "GB/s", "frac": qh_bytes / th / 1e9 / PEAK_HBM_GBS,
+                              "avg_launch_us": th * 1e6, "algorithmic_bytes": qh_bytes}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, unfused)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, unfused,
+                                           args.rot_out if (quantout or then_quant) else None)
     print(json.dumps(out), flush=True)
 
 

@@ -227,6 +227,58 @@ w8a8_status w8a8_fp8_linear_packed(const uint16_t* x, const uint8_t* w_packed, c
                                    int rot_block, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
 
+/* ---- gate/up SwiGLU whose output is quantized for the next linear -----------
+ * The down projection that follows the gate/up pair quantizes its input (the
+ * SwiGLU output h [M, N]) per token, optionally after the block-128 rotation,
+ * exactly as w8a8_quantize_act does (INT8 ConvRot card, latency-table notes).
+ * These calls produce that input -- int8 codes in the packed layout plus the
+ * per-token scales -- without writing h: the gate/up GEMM's epilogue quantizes
+ * each 128-column block of h on its own scale (one GEMM tile covers exactly
+ * one block), then a light pass rescales the blocks to the row scale.  The
+ * pages do not describe this fusion; its definition:
+ *   block b of row m (columns 128b .. 128b+127, rotated when rot_out == 128):
+ *     amax_b = max|y|, s_b = fl32(amax_b / 127), q_b = round-half-even(y / s_b);
+ *   s_tok[m] = fl32(max_b amax_b / 127)  -- equal to w8a8_quantize_act's scale;
+ *   q = round-half-even(fl32(q_b * fl32(s_b / s_tok[m])))  (0 if s_tok[m] == 0).
+ * Codes of the block holding the row's amax equal w8a8_quantize_act's; the
+ * others may differ from them by one step (a second rounding).
+ * Shapes: the gate/up GEMM's (K % 128 == 0, N % 8 == 0) and N % 64 == 0;
+ * rot_out == 128 needs N % 128 == 0.  Codes are w8a8_packed_bytes(M, N) bytes in
+ * the packed layout of a [M, N] activation (padding rows untouched): the A
+ * operand of w8a8_gemm_dequant_packed for the down projection (K = N). */
+
+/* Bytes of the block amax array [M, ceil(N / 128)] fp32 (0 for M or N <= 0). */
+size_t w8a8_block_amax_bytes(int64_t M, int64_t N);
+
+/* Workspace of w8a8_gateup_swiglu_quant_packed: w8a8_workspace_bytes(M, K)
+ * followed by the block amax array on a 256-byte boundary. */
+size_t w8a8_swiglu_quant_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/* First step alone: packed x codes + s_tok and the packed [2N, K] gate/up
+ * weight as for w8a8_gemm_swiglu_packed; writes the block codes (codes_packed)
+ * and block_amax [M, ceil(N / 128)] (row-major), and, when h is not NULL, the
+ * bf16 SwiGLU output [M, N] that was quantized. */
+w8a8_status w8a8_gemm_swiglu_blockquant_packed(const int8_t* q_packed, const float* s_tok,
+                                              const int8_t* w_gateup_packed, const float* s_ch,
+                                              const uint16_t* bias, int64_t M, int64_t N, int64_t K,
+                                              int rot_out, int8_t* codes_packed, float* block_amax,
+                                              uint16_t* h, hipStream_t stream);
+
+/* Second step alone: rescales block codes (packed [M, N], rewritten in place)
+ * to the row scale and writes s_tok [M].  N % 64 == 0. */
+w8a8_status w8a8_requantize_blocks_packed(int8_t* codes_packed, const float* block_amax, int64_t M,
+                                          int64_t N, float* s_tok, hipStream_t stream);
+
+/* Whole: quantize x (rotation rot_in), gate/up GEMM with the block-quantizing
+ * epilogue (rotation rot_out), rescale -> q_packed, s_tok.  Three kernels on
+ * `stream`; `workspace` holds w8a8_swiglu_quant_workspace_bytes(M, N, K)
+ * bytes, caller-owned. */
+w8a8_status w8a8_gateup_swiglu_quant_packed(const uint16_t* x, const int8_t* w_gateup_packed,
+                                            const float* s_ch, const uint16_t* bias, int64_t M,
+                                            int64_t N, int64_t K, int rot_in, int rot_out,
+                                            int8_t* q_packed, float* s_tok, void* workspace,
+                                            size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

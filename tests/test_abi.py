@@ -50,6 +50,11 @@ def lib():
         "w8a8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_gateup_swiglu_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_fp8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
+        "w8a8_block_amax_bytes": (SZ, [I64, I64]),
+        "w8a8_swiglu_quant_workspace_bytes": (SZ, [I64, I64, I64]),
+        "w8a8_gemm_swiglu_blockquant_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, P, P, P]),
+        "w8a8_requantize_blocks_packed": (I, [P, P, I64, I64, P, P]),
+        "w8a8_gateup_swiglu_quant_packed": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -70,7 +75,9 @@ def test_header_declares_the_documented_entry_points():
             "w8a8_packed_bytes", "w8a8_pack_weight", "w8a8_linear_packed",
             "w8a8_gateup_swiglu_packed", "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed",
             "w8a8_quantize_act_fp8_packed", "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed",
-            "w8a8_fp8_gemm_dequant_packed", "w8a8_swiglu"}
+            "w8a8_fp8_gemm_dequant_packed", "w8a8_swiglu", "w8a8_block_amax_bytes",
+            "w8a8_swiglu_quant_workspace_bytes", "w8a8_gemm_swiglu_blockquant_packed",
+            "w8a8_requantize_blocks_packed", "w8a8_gateup_swiglu_quant_packed"}
     assert want <= set(declared_symbols())
 
 
@@ -192,6 +199,39 @@ def test_pack_weight_argument_checks(lib):
     assert p(None, 0, 128, None, None) == OK      # nothing to pack
 
 
+def test_swiglu_quant_sizes_and_argument_checks(lib):
+    assert lib.w8a8_block_amax_bytes(0, 128) == 0
+    assert lib.w8a8_block_amax_bytes(3, 320) == 3 * 3 * 4          # ceil(320 / 128) blocks
+    assert lib.w8a8_block_amax_bytes(2270, 17408) == 2270 * 136 * 4
+    ws = lib.w8a8_swiglu_quant_workspace_bytes(4, 256, 512)
+    assert ws == lib.w8a8_workspace_bytes(4, 512) + 256             # 4 x 2 amax, padded to 256
+    assert lib.w8a8_swiglu_quant_workspace_bytes(0, 256, 512) == 0
+    b = lib.w8a8_gemm_swiglu_blockquant_packed
+    assert b(None, A, A, A, None, 4, 256, 512, 0, A, A, None, None) == NULLP
+    assert b(A, A, A, A, None, 4, 256, 512, 0, None, A, None, None) == NULLP
+    assert b(A, A, A, A, None, 4, 256, 512, 0, A, None, None, None) == NULLP
+    assert b(A, A, A, A, None, 4, 200, 512, 0, A, A, None, None) == SHAPE      # N % 64
+    assert b(A, A, A, A, None, 4, 320, 512, 128, A, A, None, None) == SHAPE    # rotation: N % 128
+    assert b(A, A, A, A, None, 4, 256, 512, 64, A, A, None, None) == BADARG    # rot_out
+    assert b(A, A, A, A, None, 4, 256, 320, 0, A, A, None, None) == SHAPE      # K % 128
+    assert b(A, A, A, A, None, 4, 256, 512, 0, A, A, U, None) == MISALIGNED    # h
+    assert b(None, None, None, None, None, 0, 256, 512, 0, None, None, None, None) == OK
+    r = lib.w8a8_requantize_blocks_packed
+    assert r(None, A, 4, 256, A, None) == NULLP
+    assert r(A, A, 4, 256, None, None) == NULLP
+    assert r(A, A, 4, 96, A, None) == SHAPE
+    assert r(A, A, -1, 256, A, None) == SHAPE
+    assert r(U, A, 4, 256, A, None) == MISALIGNED
+    assert r(None, None, 0, 256, None, None) == OK
+    g = lib.w8a8_gateup_swiglu_quant_packed
+    assert g(A, A, A, None, 4, 256, 512, 0, 128, A, A, A, ws - 1, None) == BADARG
+    assert g(A, A, A, None, 4, 256, 512, 3, 128, A, A, A, ws, None) == BADARG   # rot_in
+    assert g(A, A, A, None, 4, 256, 512, 0, 128, None, A, A, ws, None) == NULLP
+    assert g(A, A, A, None, 4, 256, 512, 0, 128, A, A, U, ws, None) == MISALIGNED
+    assert g(A, A, A, None, 4, 192, 512, 0, 128, A, A, A, ws, None) == SHAPE    # rotation: N % 128
+    assert g(None, None, None, None, 0, 256, 512, 0, 0, None, None, None, 0, None) == OK
+
+
 def test_valid_call_without_gpu_reports_device(lib):
     import torch
     if torch.cuda.is_available():
@@ -199,3 +239,6 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.w8a8_quantize_act(A, 4, 128, 0, A, A, None) == DEVICE
     assert lib.w8a8_gemm_i32(A, A, A, 4, 8, 128, None) == DEVICE
     assert lib.w8a8_pack_weight(A, 4, 128, A, None) == DEVICE
+    assert lib.w8a8_requantize_blocks_packed(A, A, 4, 256, A, None) == DEVICE
+    assert lib.w8a8_gemm_swiglu_blockquant_packed(A, A, A, A, None, 4, 256, 512, 128, A, A, None,
+                                                  None) == DEVICE

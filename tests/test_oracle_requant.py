@@ -71,12 +71,13 @@ def test_row_scale_step_bound_and_amax_block(N, rot):
         lo, hi = 128 * b, min(128 * b + 128, N)
         np.testing.assert_array_equal(q[m, lo:hi], q1[m, lo:hi])
         np.testing.assert_array_equal(q[m, lo:hi], qb[m, lo:hi])
-    # error of the two roundings: |q s - y| <= s/2 + s_b/2 (plus fp32 slack)
+    # error of the two roundings: |q s - y| <= s/2 + s_b/2 (plus the fp32 quotient and
+    # product errors, at most 127 * 2^-23 of a step each)
     s_b = (amax / np.float32(127)).astype(np.float64)
     sb_full = np.repeat(s_b, 128, axis=1)[:, :N]
     err = np.abs(q.astype(np.float64) * s.astype(np.float64)[:, None] - y)
     bound = 0.5 * s.astype(np.float64)[:, None] + 0.5 * sb_full
-    assert np.all(err <= bound * (1 + 1e-5))
+    assert np.all(err <= bound * (1 + 1e-4))
     # and single rounding would respect s/2: the two-step codes differ somewhere
     assert np.count_nonzero(d) > 0
 

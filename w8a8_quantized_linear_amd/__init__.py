@@ -28,7 +28,9 @@ __all__ = [
     "w8a8_gateup_swiglu", "w8a8_fp8_linear", "w8a8_linear_packed", "w8a8_gateup_swiglu_packed",
     "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed", "w8a8_quantize_act_fp8_packed",
     "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed", "w8a8_fp8_gemm_dequant_packed",
-    "w8a8_swiglu",
+    "w8a8_swiglu", "block_amax_bytes", "swiglu_quant_workspace_bytes",
+    "w8a8_gemm_swiglu_blockquant_packed", "w8a8_requantize_blocks_packed",
+    "w8a8_gateup_swiglu_quant_packed",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
@@ -62,6 +64,11 @@ _SIGS = {
     "w8a8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_gateup_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_fp8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
+    "w8a8_block_amax_bytes": (_SZ, [_I64, _I64]),
+    "w8a8_swiglu_quant_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "w8a8_gemm_swiglu_blockquant_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
+    "w8a8_requantize_blocks_packed": (_I, [_P, _P, _I64, _I64, _P, _P]),
+    "w8a8_gateup_swiglu_quant_packed": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -343,3 +350,84 @@ def w8a8_fp8_linear_packed(x, w_packed, N, s_ch, bias=None, rot_block=0, workspa
     """w8a8_fp8_linear with the E4M3FN weight [N, K] given in the packed layout."""
     return _path("w8a8_fp8_linear_packed", x, w_packed, s_ch, bias, rot_block, N, torch.uint8,
                  workspace, out, w_rows=N)
+
+
+# ------------------------ gate/up SwiGLU quantized for the next linear -------
+def block_amax_bytes(M: int, N: int) -> int:
+    return int(_lib.w8a8_block_amax_bytes(M, N))
+
+
+def swiglu_quant_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.w8a8_swiglu_quant_workspace_bytes(M, N, K))
+
+
+def w8a8_gemm_swiglu_blockquant_packed(q_packed, s_tok, w_gateup_packed, s_ch, K, bias=None,
+                                       rot_out=0, want_h=False, codes=None, amax=None):
+    """First step: returns (block codes, flat packed int8 [packed_bytes(M, N)];
+    block amax fp32 [M, ceil(N / 128)]; h bf16 [M, N] or None).  M = len(s_tok),
+    N = len(s_ch) / 2."""
+    _want(q_packed, torch.int8, "q_packed", 1)
+    _want(w_gateup_packed, torch.int8, "w_gateup_packed", 1)
+    _want(s_tok, torch.float32, "s_tok", 1)
+    _want(s_ch, torch.float32, "s_ch", 1)
+    if bias is not None:
+        _want(bias, torch.bfloat16, "bias", 1)
+    M, rows = s_tok.shape[0], s_ch.shape[0]
+    N = rows // 2
+    if q_packed.numel() < packed_bytes(M, K) or w_gateup_packed.numel() < packed_bytes(rows, K):
+        raise ValueError("inconsistent shapes")
+    if bias is not None and bias.shape[0] != rows:
+        raise ValueError("bias length must equal the weight's rows")
+    dev = q_packed.device
+    nblk = (N + 127) // 128
+    codes = codes if codes is not None else torch.empty((max(packed_bytes(M, N), 1),), dtype=torch.int8, device=dev)
+    amax = amax if amax is not None else torch.empty((M, nblk), dtype=torch.float32, device=dev)
+    if codes.numel() < packed_bytes(M, N) or amax.numel() < M * nblk:
+        raise ValueError("codes or amax too small")
+    h = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if want_h else None
+    _check(_lib.w8a8_gemm_swiglu_blockquant_packed(_ptr(q_packed), _ptr(s_tok), _ptr(w_gateup_packed),
+                                                   _ptr(s_ch), _ptr(bias), M, N, K, rot_out, _ptr(codes),
+                                                   _ptr(amax), _ptr(h), _stream()),
+           "w8a8_gemm_swiglu_blockquant_packed")
+    return codes, amax, h
+
+
+def w8a8_requantize_blocks_packed(codes, amax, M, N, s_tok=None):
+    """Second step, in place on `codes` (flat packed int8): returns s_tok fp32 [M]."""
+    _want(codes, torch.int8, "codes", 1)
+    _want(amax, torch.float32, "amax", 2)
+    if codes.numel() < packed_bytes(M, N) or tuple(amax.shape) != (M, (N + 127) // 128):
+        raise ValueError("inconsistent shapes")
+    s = s_tok if s_tok is not None else torch.empty((M,), dtype=torch.float32, device=codes.device)
+    _check(_lib.w8a8_requantize_blocks_packed(_ptr(codes), _ptr(amax), M, N, _ptr(s), _stream()),
+           "w8a8_requantize_blocks_packed")
+    return s
+
+
+def w8a8_gateup_swiglu_quant_packed(x, w_gateup_packed, N, s_ch, bias=None, rot_in=0, rot_out=0,
+                                    workspace=None, q_out=None, s_out=None):
+    """Whole: returns (packed int8 codes [packed_bytes(M, N)], s_tok fp32 [M]) of the
+    SwiGLU output, ready as the A operand of w8a8_gemm_dequant_packed (K = N)."""
+    _want(x, torch.bfloat16, "x", 2)
+    _want(w_gateup_packed, torch.int8, "w_gateup_packed", 1)
+    _want(s_ch, torch.float32, "s_ch", 1)
+    if bias is not None:
+        _want(bias, torch.bfloat16, "bias", 1)
+    M, K = x.shape
+    if w_gateup_packed.numel() < packed_bytes(2 * N, K) or s_ch.shape[0] != 2 * N:
+        raise ValueError("inconsistent shapes")
+    if bias is not None and bias.shape[0] != 2 * N:
+        raise ValueError("bias length must equal the weight's rows")
+    dev = x.device
+    need = swiglu_quant_workspace_bytes(M, N, K)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    q = q_out if q_out is not None else torch.empty((max(packed_bytes(M, N), 1),), dtype=torch.int8, device=dev)
+    s = s_out if s_out is not None else torch.empty((M,), dtype=torch.float32, device=dev)
+    if q.numel() < packed_bytes(M, N):
+        raise ValueError("q_out too small")
+    _check(_lib.w8a8_gateup_swiglu_quant_packed(_ptr(x), _ptr(w_gateup_packed), _ptr(s_ch), _ptr(bias), M, N,
+                                                K, rot_in, rot_out, _ptr(q), _ptr(s), _ptr(workspace),
+                                                workspace.numel(), _stream()),
+           "w8a8_gateup_swiglu_quant_packed")
+    return q, s

@@ -40,7 +40,9 @@
 // running tiles on one XCD share their token and weight panels in its L2.
 #include <type_traits>
 
+#include "epilogue_math.h"
 #include "internal.h"
+#include "quant_math.h"
 
 namespace w8a8 {
 namespace {
@@ -92,26 +94,6 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(u32x2 v) {
   const v4bf lo = __builtin_shufflevector(p0, p1, 0, 1, 2, 3);
   const v4bf hi = __builtin_shufflevector(p2, p3, 0, 1, 2, 3);
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// silu(g) = g * sigmoid(g), sigmoid(g) = (g >= 0 ? 1 : e) / (1 + e) with
-// e = exp(-|g|): no overflow, and very negative g gives its tiny value, not 0.
-__device__ __forceinline__ float silu_f32(float g) {
-  const float e = expf(-fabsf(g));
-  return g * ((g >= 0.0f ? 1.0f : e) / (1.0f + e));
-}
-
-__device__ __forceinline__ void bf16x4(uint2 b, float* f) {
-  f[0] = __uint_as_float(b.x << 16);
-  f[1] = __uint_as_float(b.x & 0xffff0000u);
-  f[2] = __uint_as_float(b.y << 16);
-  f[3] = __uint_as_float(b.y & 0xffff0000u);
 }
 
 // Block id -> (tile_m, tile_n): contiguous tile ranges per XCD, grouped along M.
@@ -220,12 +202,119 @@ __device__ __forceinline__ void store_tile(const Acc (&acc)[TN][TM], const float
   }
 }
 
+// kSwigluQ epilogue: the tile's 128 output columns are one block of the next
+// linear's input (its rotation block), so the tile can quantize its part of
+// every row on the block's own scale (first of the two steps that quantize the
+// SwiGLU output per token; launch_requantize_blocks is the second).
+//   1. the bf16 SwiGLU values h (as the kSwiglu epilogue computes them) go to
+//      LDS, [BM rows][128 columns], reusing the operand ring (and to qo.h when
+//      it is set); columns past N are stored as zeros;
+//   2. four lanes (a DPP quad) take a row's block, 32 values each: the exact
+//      block rotation of the quantizer (fp64 sums, one rounding to fp32) or the
+//      plain values, the block amax over the quad, s_b = amax / 127 and
+//      round-half-even codes; the codes go to the packed layout (each lane 32
+//      contiguous bytes), the amax to qo.amax[m][tile_n].
+template <int BM, int TM, int TN, int WTM, int WTN, int LDS_BYTES, typename Acc>
+__device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], const float* __restrict__ s_tok,
+                                                  const float* __restrict__ s_ch,
+                                                  const uint16_t* __restrict__ bias, const QuantOut& qo,
+                                                  int64_t M, int64_t N, int64_t mb, int64_t nb, int tile_n,
+                                                  int nblk, int wm, int wn, int frag_row, int frag_half,
+                                                  uint8_t* lds, int tid) {
+  constexpr int kStride = 128 * 2 + 16;  // LDS bytes per row of h (padding spreads the banks)
+  static_assert(BM * kStride <= LDS_BYTES, "h tile fits the operand ring");
+  __syncthreads();  // every wave is done with the operand ring
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int row_l = wm * WTM + tm * 32 + frag_row;
+    const int64_t m = mb + row_l;
+    const bool live = m < M;
+    const float st = live ? s_tok[m] : 0.0f;
+#pragma unroll
+    for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int col_l = wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half;
+        const int64_t n0 = nb + col_l;
+        uint2 hv = make_uint2(0u, 0u);
+        if (live && n0 < N) {
+          const float4 sg = *reinterpret_cast<const float4*>(s_ch + n0);
+          const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n0);
+          float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+          if (bias) {
+            bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bg);
+            bf16x4(*reinterpret_cast<const uint2*>(bias + N + n0), bu);
+          }
+          const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+          uint16_t o[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
+            const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
+            o[v] = f32_to_bf16_rne(silu_f32(g) * u);
+          }
+          hv = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+          if (qo.h) *reinterpret_cast<uint2*>(qo.h + m * N + n0) = hv;
+        }
+        *reinterpret_cast<uint2*>(lds + row_l * kStride + col_l * 2) = hv;
+      }
+  }
+  __syncthreads();
+
+  const int lane = tid & 63, p = tid & 3;
+  const int64_t kblocks = N / 64;
+#pragma unroll 1
+  for (int pass = 0; pass < BM / 64; ++pass) {
+    const int row_l = pass * 64 + tid / 4;
+    const int64_t m = mb + row_l;
+    if (m >= M) continue;  // the whole quad: one row
+    qm::u32x4 raw[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      raw[i] = *reinterpret_cast<const qm::u32x4*>(lds + row_l * kStride + p * 64 + i * 16);
+    float y[qm::kEPL];
+    if (qo.rot) {
+      qm::rotate_chunk(raw, lane, y);
+    } else {
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        y[2 * j] = qm::bf16lo(raw[j / 4][j % 4]);
+        y[2 * j + 1] = qm::bf16hi(raw[j / 4][j % 4]);
+      }
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int j = 0; j < qm::kEPL; ++j) a = fmaxf(a, fabsf(y[j]));
+    a = fmaxf(a, __shfl_xor(a, 1, 64));
+    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    const float s = a / 127.0f;  // IEEE division
+    const float r = a > 0.0f ? 1.0f / s : 0.0f;  // a zero block: r = 0 gives zero codes
+    uint32_t w[8];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {  // 8 codes at a time
+      float yv[8], k[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) yv[e] = y[8 * g + e];
+      qm::int8_codes(yv, s, r, k);
+      w[2 * g] = qm::pack_i8x4(k[0], k[1], k[2], k[3]);
+      w[2 * g + 1] = qm::pack_i8x4(k[4], k[5], k[6], k[7]);
+    }
+    const int64_t c0 = nb + 32 * p;  // first column of this lane's 32
+    if (c0 < N) {
+      uint8_t* dst = qo.codes + ((m / 32) * kblocks + c0 / 64) * 2048 + (m % 32) * 64 + (c0 % 64);
+      *reinterpret_cast<qm::u32x4*>(dst) = qm::u32x4{w[0], w[1], w[2], w[3]};
+      *reinterpret_cast<qm::u32x4*>(dst + 16) = qm::u32x4{w[4], w[5], w[6], w[7]};
+    }
+    if (p == 0) qo.amax[m * nblk + tile_n] = a;
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
           const uint8_t* __restrict__ b, const float* __restrict__ s_ch,
           const uint16_t* __restrict__ bias, void* __restrict__ out,
-          int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n) {
+          int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, QuantOut qo) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int CH = BK / 16;                       // 16-byte chunks per LDS row
   constexpr int NSUB = BK / 32;                     // 32-deep k substeps per stage
@@ -237,7 +326,9 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   static_assert(NSUB % 2 == 0 && NST >= 2, "even substeps per stage, two or more stages");
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "wave tiles of 32x32 blocks");
   static_assert(A_LOADS * NT == BM * CH && B_LOADS * NT == BN * CH, "tile / threads");
-  static_assert(EPI != Epi::kSwiglu || TN % 2 == 0, "SwiGLU needs gate/up block pairs");
+  static_assert(!paired_epi(EPI) || TN % 2 == 0, "SwiGLU needs gate/up block pairs");
+  static_assert(EPI != Epi::kSwigluQ || (BN == 256 && BM % 64 == 0 && WGM * WGN == 4),
+                "block quantization: 128 output columns per tile, 256 threads");
   static_assert(NST * LOADS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
 
@@ -250,7 +341,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   const int64_t mb = (int64_t)tile_m * BM;
   // SwiGLU tiles cover BN/2 output columns: LDS weight rows [0, BN/2) are gate
   // rows, [BN/2, BN) the matching up rows.
-  const int64_t nb = (EPI == Epi::kSwiglu) ? (int64_t)tile_n * (BN / 2) : (int64_t)tile_n * BN;
+  const int64_t nb = paired_epi(EPI) ? (int64_t)tile_n * (BN / 2) : (int64_t)tile_n * BN;
 
   // Direct-to-LDS loads: each wave instruction fills 64 consecutive 16-byte LDS
   // slots; slot p of a stage holds chunk (p % CH) ^ swizzle of tile row p / CH,
@@ -269,7 +360,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
     return (uint32_t)(rel * K + c * 16);
   };
   constexpr int ROWS_PER_LOAD = NT / CH;
-  static_assert(EPI != Epi::kSwiglu || (BN / 2) % ROWS_PER_LOAD == 0,
+  static_assert(!paired_epi(EPI) || (BN / 2) % ROWS_PER_LOAD == 0,
                 "each load instruction reads gate rows only or up rows only");
   const uint8_t* a_panel = a + mb * K;
   // SwiGLU: gate rows nb.. and up rows N + nb..; the up panel starts at the
@@ -288,7 +379,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
-    if constexpr (EPI == Epi::kSwiglu) {
+    if constexpr (paired_epi(EPI)) {
       const int64_t col = min<int64_t>(r % (BN / 2), N - 1 - nb);
       b_off[i] = src_off(r < BN / 2 ? col : up_skew + col, c, PB);
     } else {
@@ -312,7 +403,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
     for (int i = 0; i < A_LOADS; ++i) lds_dma16(a_panel + (a_off[i] + ka), st + (i * NT + wave * 64) * 16);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
-      const bool up = EPI == Epi::kSwiglu && i * ROWS_PER_LOAD >= BN / 2;  // compile-time per i
+      const bool up = paired_epi(EPI) && i * ROWS_PER_LOAD >= BN / 2;  // compile-time per i
       lds_dma16((up ? b_up_panel : b_panel) + (b_off[i] + kb), st + A_BYTES + (i * NT + wave * 64) * 16);
     }
   };
@@ -335,7 +426,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   for (int t = 0; t < TM; ++t) a_rows[t] = wm * WTM + t * 32 + frag_row;
 #pragma unroll
   for (int t = 0; t < TN; ++t) {
-    if constexpr (EPI == Epi::kSwiglu)
+    if constexpr (paired_epi(EPI))
       b_rows[t] = (t < TN / 2 ? 0 : BN / 2) + wn * (WTN / 2) + (t % (TN / 2)) * 32 + frag_row;
     else
       b_rows[t] = wn * WTN + t * 32 + frag_row;
@@ -439,22 +530,26 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   // the tail re-loads must land before the workgroup's LDS can be reused
   wait_vmcnt<0>();
 
-  store_tile<EPI, TM, TN, WTM, WTN>(acc, s_tok, s_ch, bias, out, M, N, mb, nb, wm, wn, frag_row, frag_half);
+  if constexpr (EPI == Epi::kSwigluQ)
+    swiglu_quant_tile<BM, TM, TN, WTM, WTN, NST * STAGE>(acc, s_tok, s_ch, bias, qo, M, N, mb, nb, tile_n, tiles_n, wm,
+                                            wn, frag_row, frag_half, lds, tid);
+  else
+    store_tile<EPI, TM, TN, WTM, WTN>(acc, s_tok, s_ch, bias, out, M, N, mb, nb, wm, wn, frag_row, frag_half);
 }
 
 template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
 hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const float* s_ch,
                       const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
-                      hipStream_t stream) {
+                      hipStream_t stream, const QuantOut& qo = QuantOut{}) {
   const int64_t tiles_m = (M + BM - 1) / BM;
-  const int64_t cols_per_tile = (EPI == Epi::kSwiglu) ? BN / 2 : BN;
+  const int64_t cols_per_tile = paired_epi(EPI) ? BN / 2 : BN;
   const int64_t tiles_n = (N + cols_per_tile - 1) / cols_per_tile;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL((gemm_tile<BM, BN, WGM, WGN, BK, NST, EPI, FP8, PA, PB>), dim3((unsigned)blocks),
                      dim3(64 * WGM * WGN), 0, stream, static_cast<const uint8_t*>(a), s_tok,
                      static_cast<const uint8_t*>(b), s_ch, bias, out, M, N, K, (int)tiles_m,
-                     (int)tiles_n);
+                     (int)tiles_n, qo);
   return hipGetLastError();
 }
 
@@ -471,7 +566,7 @@ template <Epi EPI, bool FP8, bool PA, bool PB>
 hipError_t launch_t(const void* a, const float* s_tok, const void* b, const float* s_ch,
                     const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
                     hipStream_t stream) {
-  const int64_t nw = (EPI == Epi::kSwiglu) ? 2 * N : N;  // weight rows
+  const int64_t nw = paired_epi(EPI) ? 2 * N : N;  // weight rows
   auto cost = [&](int bm, int bn, double eff) {
     const int64_t tiles = ((M + bm - 1) / bm) * ((nw + bn - 1) / bn);
     return (double)((tiles + kCus - 1) / kCus) * bm * bn / eff;
@@ -530,8 +625,20 @@ hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const vo
       return launch_layouts<Epi::kDequant, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
     case Epi::kSwiglu:
       return launch_layouts<Epi::kSwiglu, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+    case Epi::kSwigluQ:  // launch_gemm_swiglu_quant
+      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
+}
+
+// The 256 x 256 tile: 128 output columns per tile, one block of the next
+// linear's input.
+hipError_t launch_gemm_swiglu_quant(const void* a, const float* s_tok, const void* b,
+                                    const float* s_ch, const uint16_t* bias, const QuantOut& qo,
+                                    int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (N % 64 != 0 || (qo.rot != 0 && (qo.rot != 128 || N % 128 != 0))) return hipErrorInvalidValue;
+  return launch_cfg<256, 256, 2, 2, 64, 4, Epi::kSwigluQ, false, true, true>(a, s_tok, b, s_ch, bias, nullptr,
+                                                                          M, N, K, stream, qo);
 }
 
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream) {

@@ -58,6 +58,30 @@ __device__ __forceinline__ float int8_code(float y, float s, float r) {
   return k;
 }
 
+// Codes of n values, clamped to +-127: int8_code's fast path for all of them;
+// the IEEE quotient for those whose t lies near a half-integer, behind one
+// branch per chunk that waves almost always skip (the chunk's smallest distance
+// of |t - k| from 1/2 decides; a non-finite r, from a subnormal s, sends the
+// whole chunk down the exact path).  r = 0 (a zero scale's stand-in) gives zero
+// codes.
+template <int n>
+__device__ __forceinline__ void int8_codes(const float (&y)[n], float s, float r, float (&k)[n]) {
+  float dmin = 1.0f;
+#pragma unroll
+  for (int j = 0; j < n; ++j) {
+    const float t = y[j] * r;
+    k[j] = __builtin_rintf(t);
+    dmin = fminf(dmin, fabsf(fabsf(t - k[j]) - 0.5f));
+  }
+  if (__builtin_expect(!(dmin >= 0x1p-14f) || !(fabsf(r) <= 0x1.fffffep127f), 0)) {
+#pragma unroll
+    for (int j = 0; j < n; ++j)
+      if (!(fabsf(fabsf(y[j] * r - k[j]) - 0.5f) >= 0x1p-14f)) k[j] = __builtin_rintf(y[j] / s);
+  }
+#pragma unroll
+  for (int j = 0; j < n; ++j) k[j] = fminf(fmaxf(k[j], -127.0f), 127.0f);
+}
+
 // Exact rotation of one 32-element chunk: the lane holds elements 32p .. 32p+31
 // of a 128-block, p = lane % 4 (its position in a DPP quad whose other lanes
 // hold the rest of the block).  Block sums of the bf16 values are formed in

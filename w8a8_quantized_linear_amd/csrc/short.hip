@@ -27,6 +27,7 @@
 // quantization costs less than a kernel launch.
 #include <type_traits>
 
+#include "epilogue_math.h"
 #include "internal.h"
 #include "quant_math.h"
 
@@ -56,23 +57,6 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-__device__ __forceinline__ float silu_f32(float g) {
-  const float e = expf(-fabsf(g));
-  return g * ((g >= 0.0f ? 1.0f : e) / (1.0f + e));
-}
-
-__device__ __forceinline__ void bf16x4(uint2 b, float* f) {
-  f[0] = __uint_as_float(b.x << 16);
-  f[1] = __uint_as_float(b.x & 0xffff0000u);
-  f[2] = __uint_as_float(b.y << 16);
-  f[3] = __uint_as_float(b.y & 0xffff0000u);
-}
 
 template <Epi EPI, bool ROT, bool PB>
 __global__ void __launch_bounds__(256)
@@ -256,7 +240,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
         const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
         uint16_t o[4];
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = bf16_rne(__builtin_fmaf((float)acc[t][4 * q + v], st * scv[v], bv[v]));
+        for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_rne(__builtin_fmaf((float)acc[t][4 * q + v], st * scv[v], bv[v]));
         *reinterpret_cast<uint2*>(yrow + n0) =
             make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
       }
@@ -278,7 +262,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
       for (int v = 0; v < 4; ++v) {
         const float g = __builtin_fmaf((float)acc[0][4 * q + v], st * sgv[v], bg[v]);
         const float u = __builtin_fmaf((float)acc[1][4 * q + v], st * suv[v], bu[v]);
-        o[v] = bf16_rne(silu_f32(g) * u);
+        o[v] = f32_to_bf16_rne(silu_f32(g) * u);
       }
       *reinterpret_cast<uint2*>(yrow + n0) =
           make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));

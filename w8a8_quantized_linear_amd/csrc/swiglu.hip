@@ -4,9 +4,8 @@
 //
 // What it computes: y[m][n] = bf16(silu(g) * u) with g = gate[m][n] and
 // u = up[m][n] the bf16 outputs of the two projections, evaluated in fp32 with
-// the same formula as the fused epilogue -- silu(g) = g * sigmoid(g) with
-// sigmoid(g) = (g >= 0 ? 1 : e) / (1 + e), e = exp(-|g|), which never overflows,
-// so very negative gates give the tiny (not zero) values they should -- and one
+// the same SiLU as the fused epilogue (silu_f32: sigmoid(g) = (g >= 0 ? 1 : e) /
+// (1 + e) with e = exp(-|g|), which never overflows) and one
 // round-to-nearest-even to bf16.
 //
 // Design: HBM bound (4 bytes read, 2 written per element).  One thread per 8
@@ -14,6 +13,7 @@
 // covers 512 contiguous output elements.  gate and up rows are `ld` elements
 // apart (the two halves of one [M, 2N] projection, or two separate [M, N]
 // tensors with ld = N).
+#include "epilogue_math.h"
 #include "internal.h"
 
 namespace w8a8 {
@@ -21,23 +21,12 @@ namespace {
 
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float silu_f32(float g) {
-  const float e = expf(-fabsf(g));
-  return g * ((g >= 0.0f ? 1.0f : e) / (1.0f + e));
-}
-
 __device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
   const float g0 = __uint_as_float(gw << 16), g1 = __uint_as_float(gw & 0xffff0000u);
   const float u0 = __uint_as_float(uw << 16), u1 = __uint_as_float(uw & 0xffff0000u);
   const float y0 = silu_f32(g0) * u0;
   const float y1 = silu_f32(g1) * u1;
-  return f32_to_bf16_rne(y0) | (f32_to_bf16_rne(y1) << 16);
+  return (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
 }
 
 __global__ void __launch_bounds__(256)
