@@ -2,7 +2,7 @@
 // the W8A8 path).
 //
 // What it computes: acc[m][n] = sum_k a[m][k] * b[n][k] over int8 codes (exact
-// int32) or E4M3FN codes (fp32 accumulation), followed in registers by
+// int32) or E4M3FN codes (fp32 accumulation), followed by
 //   kRawI32 : acc as int32;
 //   kDequant: bf16(acc * s_tok[m] * s_ch[n] + bias[n])  -- the scale and bias
 //             fusion of the INT8 GEMM epilogue ("CLEF Calibrated INT8 ConvRot"
@@ -309,6 +309,87 @@ __device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], cons
   }
 }
 
+// bf16 epilogues (kDequant, kSwiglu) staged through LDS.  In the MFMA layout a
+// lane holds 4 consecutive columns of one row, so a direct store instruction
+// writes 16 bytes into each of 32 rows -- 32 partial cache lines per
+// instruction, which held the output to ~1 TB/s (a 1,502 x 4,096 GEMM at K = 128
+// took 13 us).  Instead each wave writes its (WTM x COLS) bf16 sub-tile into its
+// own LDS region (rows of COLS * 2 bytes, 16-byte chunks XOR-swizzled by row so
+// the 32 rows of a write spread over the banks), then reads it back 16 bytes
+// per lane with consecutive lanes along a row, so each store instruction
+// covers 64 / (COLS / 8) whole row segments.  The caller has made sure that no
+// wave still reads the operand ring (barrier) and passes this wave's region.
+template <Epi EPI, int TM, int TN, int WTM, int WTN, typename Acc>
+__device__ __forceinline__ void store_tile_staged(const Acc (&acc)[TN][TM], const float* __restrict__ s_tok,
+                                                  const float* __restrict__ s_ch,
+                                                  const uint16_t* __restrict__ bias, uint16_t* __restrict__ out,
+                                                  int64_t M, int64_t N, int64_t mb, int64_t nb, int wm, int wn,
+                                                  int frag_row, int frag_half, uint8_t* region, int lane) {
+  constexpr int COLS = EPI == Epi::kSwiglu ? WTN / 2 : WTN;  // output columns of the wave's sub-tile
+  constexpr int TNO = COLS / 32;                              // 32-column output blocks
+  constexpr int ROWB = COLS * 2;                              // bytes per staged row
+  constexpr int CPR = ROWB / 16;                              // 16-byte chunks per row
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 4, 8 or 16 chunks");
+  const int64_t m0 = mb + (int64_t)wm * WTM, n0w = nb + (int64_t)wn * COLS;
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const int row = tm * 32 + frag_row;
+    const int64_t m = m0 + row;
+    const float st = m < M ? s_tok[m] : 0.0f;
+#pragma unroll
+    for (int tn = 0; tn < TNO; ++tn)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int nl = tn * 32 + 8 * q + 4 * frag_half;  // column within the sub-tile
+        const int64_t n = n0w + nl;
+        uint2 hv = make_uint2(0u, 0u);
+        if (m < M && n < N) {
+          uint16_t o[4];
+          if constexpr (EPI == Epi::kDequant) {
+            const float4 sc = *reinterpret_cast<const float4*>(s_ch + n);
+            float bv[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) bf16x4(*reinterpret_cast<const uint2*>(bias + n), bv);
+            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+              o[v] = f32_to_bf16_rne(__builtin_fmaf((float)acc[tn][tm][4 * q + v], st * scv[v], bv[v]));
+          } else {  // gate block tn, up block tn + TN/2
+            const float4 sg = *reinterpret_cast<const float4*>(s_ch + n);
+            const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n);
+            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
+            if (bias) {
+              bf16x4(*reinterpret_cast<const uint2*>(bias + n), bg);
+              bf16x4(*reinterpret_cast<const uint2*>(bias + N + n), bu);
+            }
+            const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+              const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
+              const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
+              o[v] = f32_to_bf16_rne(silu_f32(g) * u);
+            }
+          }
+          hv = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+        }
+        const int chunk = nl / 8;  // 16-byte chunk of the row; the lane's 8 bytes are its half frag_half
+        *reinterpret_cast<uint2*>(region + row * ROWB + ((chunk ^ (row % CPR)) * 16) + 8 * frag_half) = hv;
+      }
+  }
+  // (LDS accesses of one wave complete in order; the wave barrier keeps the
+  // compiler from moving the reads above the writes)
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  constexpr int RPI = 64 / CPR;  // rows per store instruction
+  const int c = lane % CPR;
+#pragma unroll
+  for (int r0 = 0; r0 < WTM; r0 += RPI) {
+    const int row = r0 + lane / CPR;
+    const int64_t m = m0 + row, n = n0w + c * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * ROWB + ((c ^ (row % CPR)) * 16));
+    if (m < M && n < N) *reinterpret_cast<u32x4*>(out + m * N + n) = v;
+  }
+}
+
 template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
 __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
@@ -432,10 +513,11 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
       b_rows[t] = wn * WTN + t * 32 + frag_row;
   }
 
-  // Two fragment register sets, alternating by substep: the next substep's
-  // fragments are read from LDS while the current one's MFMAs run.  (Set
-  // indices are compile-time constants so the arrays stay in registers.)
-  v4i fa[2][TM], fb[2][TN];
+  // Fragment register sets for two stages (set indices are compile-time
+  // constants so the arrays stay in registers): a whole stage's fragments are
+  // read from LDS one stage ahead of its MFMAs.  (Reading only one substep
+  // ahead measured 1-2% slower on every workload.)
+  v4i fa[2 * NSUB][TM], fb[2 * NSUB][TN];
   auto read_frags = [&](auto set_c, int64_t step, int sub) __attribute__((always_inline)) {
     constexpr int set = decltype(set_c)::value;
     const uint8_t* la = lds + (int)(step % NST) * STAGE;
@@ -472,13 +554,16 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
     }
   };
 
-  // Stage s lives in LDS buffer s % NST.  Stages 0 .. NST-1 are issued up front.
-  // In stage k, after substep NSUB-2 -- by then every read of stage k has been
-  // issued -- the wave waits until stage k + 1 has landed (its own loads:
-  // vmcnt; everyone's: the barrier), then refills buffer k % NST with stage
-  // k + NST while the last substep runs.  With one wave per SIMD any non-MFMA
-  // instruction between MFMAs idles the matrix core, so LDS reads and loads are
-  // interleaved one per MFMA (sched_group_barrier).
+  // Stage s lives in LDS buffer s % NST; stages 0 .. NST-1 are issued up front.
+  // Stage k's fragments are read during stage k - 1 (stage 0's after the
+  // prologue).  At the start of stage k the wave waits until stage k + 1 has
+  // landed (own loads: vmcnt) and its reads of stage k are done (lgkmcnt); the
+  // barrier then makes both hold for every wave, so buffer k % NST is refilled
+  // with stage k + NST and stage k + 1 is read while stage k is multiplied.
+  // Stages come in pairs (K / BK even), so each stage's register sets are
+  // fixed at compile time.  With one wave per SIMD any non-MFMA instruction
+  // between MFMAs idles the matrix core, so LDS reads and loads are interleaved
+  // one per MFMA (sched_group_barrier).
   constexpr int NMFMA = TM * TN * (FP8 ? 2 : 1);   // MFMAs per substep
   constexpr int NREAD = TM + TN;                    // ds_read_b128 per substep
   constexpr int RD_PER = (NREAD + NMFMA - 1) / NMFMA;            // LDS reads per MFMA slot
@@ -488,53 +573,48 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   wait_vmcnt<(NST - 1) * LOADS>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
-  read_frags(std::integral_constant<int, 0>{}, 0, 0);
-
-  for (int64_t ks = 0; ks < ksteps; ++ks) {
-    static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
-      constexpr int j = decltype(j_c)::value;
-      constexpr int cur = j & 1;
-      if constexpr (j < NSUB - 1) {
-        // prefetch substep j + 1 of this stage while multiplying substep j
-        read_frags(std::integral_constant<int, cur ^ 1>{}, ks, j + 1);
-        mfmas(std::integral_constant<int, cur>{});
+  static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
+    read_frags(std::integral_constant<int, decltype(j_c)::value>{}, 0, decltype(j_c)::value);
+  });
+  for (int64_t ks = 0; ks < ksteps; ks += 2) {
+    static_for<0, 2>([&](auto p_c) __attribute__((always_inline)) {
+      constexpr int p = decltype(p_c)::value;
+      const int64_t k = ks + p;
+      wait_vmcnt<(NST - 2) * LOADS>();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
+        constexpr int j = decltype(j_c)::value;
+        if constexpr (j == 0) issue(k + NST);
+        read_frags(std::integral_constant<int, (1 - p) * NSUB + j>{}, k + 1, j);
+        mfmas(std::integral_constant<int, p * NSUB + j>{});
 #pragma unroll
         for (int i = 0; i < NMFMA; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, j);       // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x100, RD_PER, j);  // LDS reads
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, j);  // one MFMA
+          // LDS reads, plus in the first substep the stage's loads
+          __builtin_amdgcn_sched_group_barrier(j == 0 ? 0x120 : 0x100, j == 0 ? MEM_PER : RD_PER, j);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (j == NSUB - 2) {
-          // every read of stage ks is issued; stage ks + 1 landed (stages
-          // ks + 2 .. ks + NST - 1 may still be in flight); then everyone's
-          wait_vmcnt<(NST - 2) * LOADS>();
-          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-          __builtin_amdgcn_s_barrier();
-          asm volatile("" ::: "memory");
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      } else {
-        // last substep: refill buffer ks % NST, prefetch substep 0 of the next stage
-        issue(ks + NST);
-        read_frags(std::integral_constant<int, cur ^ 1>{}, ks + 1, 0);
-        mfmas(std::integral_constant<int, cur>{});
-#pragma unroll
-        for (int i = 0; i < NMFMA; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, j);        // one MFMA
-          __builtin_amdgcn_sched_group_barrier(0x120, MEM_PER, j);  // LDS reads, loads
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      });
     });
   }
   // the tail re-loads must land before the workgroup's LDS can be reused
   wait_vmcnt<0>();
 
-  if constexpr (EPI == Epi::kSwigluQ)
+  if constexpr (EPI == Epi::kSwigluQ) {
     swiglu_quant_tile<BM, TM, TN, WTM, WTN, NST * STAGE>(acc, s_tok, s_ch, bias, qo, M, N, mb, nb, tile_n, tiles_n, wm,
                                             wn, frag_row, frag_half, lds, tid);
-  else
+  } else if constexpr (EPI == Epi::kRawI32) {
     store_tile<EPI, TM, TN, WTM, WTN>(acc, s_tok, s_ch, bias, out, M, N, mb, nb, wm, wn, frag_row, frag_half);
+  } else {
+    constexpr int REGION = WTM * (EPI == Epi::kSwiglu ? WTN / 2 : WTN) * 2;
+    static_assert(REGION * WGM * WGN <= NST * STAGE, "staged output fits the operand ring");
+    __syncthreads();  // every wave is done with the operand ring
+    store_tile_staged<EPI, TM, TN, WTM, WTN>(acc, s_tok, s_ch, bias, static_cast<uint16_t*>(out), M, N, mb, nb,
+                                             wm, wn, frag_row, frag_half, lds + wave * REGION, lane);
+  }
 }
 
 template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
@@ -546,6 +626,7 @@ hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const fl
   const int64_t tiles_n = (N + cols_per_tile - 1) / cols_per_tile;
   const int64_t blocks = tiles_m * tiles_n;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  if ((K / BK) % 2 != 0) return hipErrorInvalidValue;  // stages come in pairs
   hipLaunchKernelGGL((gemm_tile<BM, BN, WGM, WGN, BK, NST, EPI, FP8, PA, PB>), dim3((unsigned)blocks),
                      dim3(64 * WGM * WGN), 0, stream, static_cast<const uint8_t*>(a), s_tok,
                      static_cast<const uint8_t*>(b), s_ch, bias, out, M, N, K, (int)tiles_m,
