@@ -81,7 +81,7 @@ def parse():
 
 def kernel_sources_digest() -> str:
     h = hashlib.sha256()
-    for name in ("gemm.hip", "quantize.hip", "internal.h"):
+    for name in ("gemm.hip", "quantize.hip", "internal.h", "epilogue_math.h", "quant_math.h"):
         h.update((ROOT / "w8a8_quantized_linear_amd" / "csrc" / name).read_bytes())
     return h.hexdigest()[:16]
 
