@@ -127,78 +127,27 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
 }
 
-// Epilogue of one wave's (TM x TN) 32x32 blocks, in registers.  32x32 block
-// layout: lane l holds token column l % 32 and, in registers 4q .. 4q+3, weight
-// rows 8q + 4 * (l / 32) + 0..3 of the block.
-template <Epi EPI, int TM, int TN, int WTM, int WTN, typename Acc>
-__device__ __forceinline__ void store_tile(const Acc (&acc)[TN][TM], const float* __restrict__ s_tok,
-                                           const float* __restrict__ s_ch,
-                                           const uint16_t* __restrict__ bias, void* __restrict__ out,
-                                           int64_t M, int64_t N, int64_t mb, int64_t nb, int wm, int wn,
-                                           int frag_row, int frag_half) {
+// Raw int32 epilogue of one wave's (TM x TN) 32x32 blocks, stored from
+// registers (the int32 output exists for the exactness tests only).  32x32
+// block layout: lane l holds token column l % 32 and, in registers 4q .. 4q+3,
+// weight rows 8q + 4 * (l / 32) + 0..3 of the block.
+template <int TM, int TN, int WTM, int WTN, typename Acc>
+__device__ __forceinline__ void store_tile_i32(const Acc (&acc)[TN][TM], int32_t* __restrict__ out, int64_t M,
+                                               int64_t N, int64_t mb, int64_t nb, int wm, int wn, int frag_row,
+                                               int frag_half) {
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int64_t m = mb + wm * WTM + tm * 32 + frag_row;
     if (m >= M) continue;
-    if constexpr (EPI == Epi::kRawI32) {
 #pragma unroll
-      for (int tn = 0; tn < TN; ++tn)
+    for (int tn = 0; tn < TN; ++tn)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int64_t n0 = nb + wn * WTN + tn * 32 + 8 * q + 4 * frag_half;
-          if (n0 >= N) continue;
-          const v16i& v = reinterpret_cast<const v16i&>(acc[tn][tm]);
-          *reinterpret_cast<int4*>(static_cast<int32_t*>(out) + m * N + n0) =
-              make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        }
-    } else {
-      const float st = s_tok[m];
-      uint16_t* yrow = static_cast<uint16_t*>(out) + m * N;
-      if constexpr (EPI == Epi::kDequant) {
-#pragma unroll
-        for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n0 = nb + wn * WTN + tn * 32 + 8 * q + 4 * frag_half;
-            if (n0 >= N) continue;
-            const float4 sc = *reinterpret_cast<const float4*>(s_ch + n0);
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bv);
-            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-            uint16_t o[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v)
-              o[v] = f32_to_bf16_rne(__builtin_fmaf((float)acc[tn][tm][4 * q + v], st * scv[v], bv[v]));
-            *reinterpret_cast<uint2*>(yrow + n0) =
-                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-          }
-      } else {  // kSwiglu: blocks [0, TN/2) are gate, [TN/2, TN) the matching up rows
-#pragma unroll
-        for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t n0 = nb + wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half;  // output column
-            if (n0 >= N) continue;
-            const float4 sg = *reinterpret_cast<const float4*>(s_ch + n0);
-            const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n0);
-            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) {
-              bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bg);
-              bf16x4(*reinterpret_cast<const uint2*>(bias + N + n0), bu);
-            }
-            const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
-            uint16_t o[4];
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
-              const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
-              o[v] = f32_to_bf16_rne(silu_f32(g) * u);
-            }
-            *reinterpret_cast<uint2*>(yrow + n0) =
-                make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-          }
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n0 = nb + wn * WTN + tn * 32 + 8 * q + 4 * frag_half;
+        if (n0 >= N) continue;
+        const v16i& v = reinterpret_cast<const v16i&>(acc[tn][tm]);
+        *reinterpret_cast<int4*>(out + m * N + n0) = make_int4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
       }
-    }
   }
 }
 
@@ -607,7 +556,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
     swiglu_quant_tile<BM, TM, TN, WTM, WTN, NST * STAGE>(acc, s_tok, s_ch, bias, qo, M, N, mb, nb, tile_n, tiles_n, wm,
                                             wn, frag_row, frag_half, lds, tid);
   } else if constexpr (EPI == Epi::kRawI32) {
-    store_tile<EPI, TM, TN, WTM, WTN>(acc, s_tok, s_ch, bias, out, M, N, mb, nb, wm, wn, frag_row, frag_half);
+    store_tile_i32<TM, TN, WTM, WTN>(acc, static_cast<int32_t*>(out), M, N, mb, nb, wm, wn, frag_row, frag_half);
   } else {
     constexpr int REGION = WTM * (EPI == Epi::kSwiglu ? WTN / 2 : WTN) * 2;
     static_assert(REGION * WGM * WGN <= NST * STAGE, "staged output fits the operand ring");
