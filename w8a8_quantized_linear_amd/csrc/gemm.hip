@@ -28,7 +28,7 @@
 // ops, so large wave tiles need less LDS bandwidth per MFMA.  K advances BK = 64
 // bytes per stage through a ring of NST LDS buffers filled by direct-to-LDS
 // loads (global_load_lds_dwordx4: no staging registers, no LDS write
-// instructions), issued NST - 1 stages ahead of use; one barrier per stage.
+// instructions), issued NST - 2 stages ahead of use; one barrier per stage.
 // LDS rows are XOR-swizzled in 16-byte units so the MFMA operand reads are
 // bank-conflict free.  Operands may be row-major or in the packed layout of
 // 32-row x 64-byte blocks, in which every 32 rows of a stage are one contiguous
@@ -353,7 +353,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   constexpr int A_LOADS = BM * CH / NT, B_LOADS = BN * CH / NT;
   constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
   constexpr int LOADS = A_LOADS + B_LOADS;          // per thread per stage
-  static_assert(NSUB % 2 == 0 && NST >= 2, "even substeps per stage, two or more stages");
+  static_assert(NSUB % 2 == 0 && NST >= 3, "even substeps per stage, three or more stages");
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "wave tiles of 32x32 blocks");
   static_assert(A_LOADS * NT == BM * CH && B_LOADS * NT == BN * CH, "tile / threads");
   static_assert(!paired_epi(EPI) || TN % 2 == 0, "SwiGLU needs gate/up block pairs");
@@ -503,23 +503,27 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
     }
   };
 
-  // Stage s lives in LDS buffer s % NST; stages 0 .. NST-1 are issued up front.
+  // Stage s lives in LDS buffer s % NST; stages 0 .. NST-2 are issued up front.
   // Stage k's fragments are read during stage k - 1 (stage 0's after the
   // prologue).  At the start of stage k the wave waits until stage k + 1 has
-  // landed (own loads: vmcnt) and its reads of stage k are done (lgkmcnt); the
-  // barrier then makes both hold for every wave, so buffer k % NST is refilled
-  // with stage k + NST and stage k + 1 is read while stage k is multiplied.
-  // Stages come in pairs (K / BK even), so each stage's register sets are
-  // fixed at compile time.  With one wave per SIMD any non-MFMA instruction
-  // between MFMAs idles the matrix core, so LDS reads and loads are interleaved
-  // one per MFMA (sched_group_barrier).
+  // landed (own loads: vmcnt) and the barrier makes that hold for every wave;
+  // then stage k + NST - 1 is loaded into buffer (k - 1) % NST, the buffer of
+  // stage k - 1, whose fragment reads every wave has completed (its MFMAs ran
+  // before the barrier), and stage k + 1 is read while stage k is multiplied.
+  // (Refilling the buffer of stage k instead needs an LDS-read drain before the
+  // barrier: 6% slower at 192 x 128 on uniformly random codes, the same at
+  // 256 x 256 and within 1% on the workloads' own data.)  Stages come in
+  // pairs (K / BK even), so each stage's register sets are fixed at compile
+  // time.  With one wave per SIMD any non-MFMA instruction between MFMAs idles
+  // the matrix core, so LDS reads and loads are interleaved one per MFMA
+  // (sched_group_barrier).
   constexpr int NMFMA = TM * TN * (FP8 ? 2 : 1);   // MFMAs per substep
   constexpr int NREAD = TM + TN;                    // ds_read_b128 per substep
   constexpr int RD_PER = (NREAD + NMFMA - 1) / NMFMA;            // LDS reads per MFMA slot
   constexpr int MEM_PER = (NREAD + LOADS + NMFMA - 1) / NMFMA;   // reads + loads per MFMA slot
 #pragma unroll
-  for (int s = 0; s < NST; ++s) issue(s);
-  wait_vmcnt<(NST - 1) * LOADS>();
+  for (int s = 0; s < NST - 1; ++s) issue(s);
+  wait_vmcnt<(NST - 2) * LOADS>();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
@@ -529,14 +533,13 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
     static_for<0, 2>([&](auto p_c) __attribute__((always_inline)) {
       constexpr int p = decltype(p_c)::value;
       const int64_t k = ks + p;
-      wait_vmcnt<(NST - 2) * LOADS>();
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      wait_vmcnt<(NST - 3) * LOADS>();
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
       static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
         constexpr int j = decltype(j_c)::value;
-        if constexpr (j == 0) issue(k + NST);
+        if constexpr (j == 0) issue(k + NST - 1);
         read_frags(std::integral_constant<int, (1 - p) * NSUB + j>{}, k + 1, j);
         mfmas(std::integral_constant<int, p * NSUB + j>{});
 #pragma unroll
