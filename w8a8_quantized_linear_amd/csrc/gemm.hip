@@ -238,16 +238,10 @@ __device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], cons
     a = fmaxf(a, __shfl_xor(a, 2, 64));
     const float s = a / 127.0f;  // IEEE division
     const float r = a > 0.0f ? 1.0f / s : 0.0f;  // a zero block: r = 0 gives zero codes
+    const bool fast = qm::fast_quotient_ok(s);
     uint32_t w[8];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {  // 8 codes at a time
-      float yv[8], k[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) yv[e] = y[8 * g + e];
-      qm::int8_codes(yv, s, r, k);
-      w[2 * g] = qm::pack_i8x4(k[0], k[1], k[2], k[3]);
-      w[2 * g + 1] = qm::pack_i8x4(k[4], k[5], k[6], k[7]);
-    }
+    for (int g = 0; g < 8; ++g) w[g] = qm::int8_codes4(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3], s, r, fast);
     const int64_t c0 = nb + 32 * p;  // first column of this lane's 32
     if (c0 < N) {
       uint8_t* dst = qo.codes + ((m / 32) * kblocks + c0 / 64) * 2048 + (m % 32) * 64 + (c0 % 64);

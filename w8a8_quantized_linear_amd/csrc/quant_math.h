@@ -40,46 +40,45 @@ __device__ __forceinline__ double quad_xor(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
-__device__ __forceinline__ uint32_t pack_i8x4(float a, float b, float c, float d) {
-  uint32_t ia = (uint32_t)(int)a & 0xffu, ib = (uint32_t)(int)b & 0xffu;
-  uint32_t ic = (uint32_t)(int)c & 0xffu, id = (uint32_t)(int)d & 0xffu;
-  return ia | (ib << 8) | (ic << 16) | (id << 24);
+// int8 codes.  The code of y is round-half-even(fl32(y / s)) (|y| <= amax, so
+// |y / s| <= 127 * (1 + 2^-23) and no clamp is ever needed).  With
+// r = fl32(1/s) correctly rounded, t = fl32(y * r) lies within one ulp of y / s,
+// so e = y - t * s is exact in one FMA and fl32(t + e * r) is the correctly
+// rounded quotient (Markstein's theorem for a correctly rounded reciprocal;
+// also checked against the IEEE division on 1.7e10 random and near-tie pairs,
+// no difference).  This needs the residual e in the normal range wherever the
+// rounding can matter (|y / s| >= 1/2): s >= 2^-100 is enough; smaller scales
+// take the IEEE division.  Adding 1.5 * 2^23 to the quotient rounds it to an
+// integer, half to even, in the low bits of its representation, whose low
+// byte is the two's-complement code.
+constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+
+// True when the fast exact quotient applies to this scale (s = 0, with r = 0,
+// gives zero codes).
+__device__ __forceinline__ bool fast_quotient_ok(float s) { return s >= 0x1p-100f || s == 0.0f; }
+
+// Low byte = code of y (the result's bits; see above).
+__device__ __forceinline__ uint32_t code_bits(float y, float s, float r, bool fast) {
+  float q;
+  if (fast) {
+    const float t = y * r;
+    q = __builtin_fmaf(__builtin_fmaf(-t, s, y), r, t);
+  } else {
+    q = y / s;  // IEEE division (uniform per row; never taken for realistic scales)
+  }
+  return __float_as_uint(q + kRoundMagic);
 }
 
-// Code of fl32(y / s) rounded half to even, via the reciprocal r = fl32(1/s).
-__device__ __forceinline__ float int8_code(float y, float s, float r) {
-  const float t = y * r;
-  const float k = __builtin_rintf(t);
-  // |t - y/s| <= 2^-16 and |fl32(y/s) - y/s| <= 2^-18 for |y/s| < 128: only a t
-  // within 2^-15 of a half-integer can round differently from the IEEE
-  // quotient.  (Written so that a non-finite t, from a subnormal s, also takes
-  // the exact path.)
-  if (__builtin_expect(!(fabsf(fabsf(t - k) - 0.5f) >= 0x1p-14f), 0)) return __builtin_rintf(y / s);
-  return k;
-}
-
-// Codes of n values, clamped to +-127: int8_code's fast path for all of them;
-// the IEEE quotient for those whose t lies near a half-integer, behind one
-// branch per chunk that waves almost always skip (the chunk's smallest distance
-// of |t - k| from 1/2 decides; a non-finite r, from a subnormal s, sends the
-// whole chunk down the exact path).  r = 0 (a zero scale's stand-in) gives zero
-// codes.
-template <int n>
-__device__ __forceinline__ void int8_codes(const float (&y)[n], float s, float r, float (&k)[n]) {
-  float dmin = 1.0f;
-#pragma unroll
-  for (int j = 0; j < n; ++j) {
-    const float t = y[j] * r;
-    k[j] = __builtin_rintf(t);
-    dmin = fminf(dmin, fabsf(fabsf(t - k[j]) - 0.5f));
-  }
-  if (__builtin_expect(!(dmin >= 0x1p-14f) || !(fabsf(r) <= 0x1.fffffep127f), 0)) {
-#pragma unroll
-    for (int j = 0; j < n; ++j)
-      if (!(fabsf(fabsf(y[j] * r - k[j]) - 0.5f) >= 0x1p-14f)) k[j] = __builtin_rintf(y[j] / s);
-  }
-#pragma unroll
-  for (int j = 0; j < n; ++j) k[j] = fminf(fmaxf(k[j], -127.0f), 127.0f);
+// Four codes packed as int8 bytes (byte i = code of y_i).
+__device__ __forceinline__ uint32_t int8_codes4(float y0, float y1, float y2, float y3, float s, float r,
+                                               bool fast) {
+  const uint32_t u0 = code_bits(y0, s, r, fast), u1 = code_bits(y1, s, r, fast);
+  const uint32_t u2 = code_bits(y2, s, r, fast), u3 = code_bits(y3, s, r, fast);
+  // v_perm_b32 selectors: 0..3 pick bytes of the second operand, 4..7 of the
+  // first, 0x0c gives 0x00
+  const uint32_t lo = __builtin_amdgcn_perm(u1, u0, 0x0c0c0400u);  // [u0.b0, u1.b0, 0, 0]
+  const uint32_t hi = __builtin_amdgcn_perm(u3, u2, 0x04000c0cu);  // [0, 0, u2.b0, u3.b0]
+  return lo | hi;
 }
 
 // Exact rotation of one 32-element chunk: the lane holds elements 32p .. 32p+31

@@ -22,10 +22,10 @@
 //     fl64(2^-3.5) and rounded once to fp32.  The codes are therefore those of
 //     the exactly rotated row.
 //   * amax by wave butterfly plus an LDS step across the row's waves.
-//   * int8 codes: t = y * fl32(1/s), k = rint(t).  t is within 2 ulps of the
-//     IEEE quotient y / s, so k is the code of fl32(y / s) unless t lies within
-//     a few ulps of a half-integer; those rare elements are redone with the
-//     IEEE division (behind one branch per 8 codes).  E4M3FN codes use the IEEE division and the hardware RNE
+//   * int8 codes: the exact quotient fl32(y / s) from r = fl32(1/s) with one
+//     multiply and two FMAs (a correctly rounded reciprocal makes one
+//     correction step exact), rounded half to even by adding 1.5 * 2^23; no
+//     branch, no clamp (quant_math.h states the argument).  E4M3FN codes use the IEEE division and the hardware RNE
 //     converter after clamping to +-448.
 //   * Code stores, row-major or in the GEMM's packed layout (blocks of 32 rows
 //     x 64 bytes, block (r / 32, k / 64) at byte ((r / 32) * (K / 64) + k / 64)
@@ -127,6 +127,7 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
   if (tid == 0) s_out[row] = s;
   const bool zero_row = !(amax > 0.0f);
   const float r = zero_row ? 0.0f : 1.0f / s;
+  const bool fast = fast_quotient_ok(s);
 
   // element e of this row (e % 8 == 0) goes to qr + (e & ~63) * kstride + (e & 63)
   uint8_t* qr = q + (packed ? (row / 32) * 32 * (int64_t)K + (row % 32) * 64 : row * (int64_t)K);
@@ -134,13 +135,6 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
   // codes of the 8 elements of piece v of chunk i, as two 32-bit words (codes are
   // formed per piece, so that only 8 of them are live at a time)
   auto encode8 = [&](int i, int v, uint32_t* out) __attribute__((always_inline)) {
-    float kc[8];
-    if constexpr (!FP8) {
-      float yv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) yv[e] = y[i][8 * v + e];
-      int8_codes(yv, s, r, kc);  // (r = 0 for a zero row: zero codes)
-    }
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       float t[4];
@@ -154,7 +148,8 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], wd, true);
         out[g] = (uint32_t)wd;
       } else {
-        out[g] = pack_i8x4(kc[4 * g], kc[4 * g + 1], kc[4 * g + 2], kc[4 * g + 3]);
+        const float* yg = &y[i][8 * v + 4 * g];
+        out[g] = int8_codes4(yg[0], yg[1], yg[2], yg[3], s, r, fast);  // (r = 0 for a zero row: zero codes)
       }
     }
   };

@@ -150,6 +150,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
     const float s = amax / 127.0f;             // IEEE division
     const bool zero_row = !(amax > 0.0f);
     const float rcp = zero_row ? 0.0f : 1.0f / s;
+    const bool fast = fast_quotient_ok(s);
     const bool write_ws = tile_n == 0 && live;
     if (q == 0) {
       s_rows[r] = s;
@@ -162,15 +163,8 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
       if (c >= nchunks) continue;
       uint32_t wd[8];
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        float t[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float k = zero_row ? 0.0f : int8_code(v[i][4 * g + e], s, rcp);
-          t[e] = fminf(fmaxf(k, -127.0f), 127.0f);
-        }
-        wd[g] = pack_i8x4(t[0], t[1], t[2], t[3]);
-      }
+      for (int g = 0; g < 8; ++g)
+        wd[g] = int8_codes4(v[i][4 * g], v[i][4 * g + 1], v[i][4 * g + 2], v[i][4 * g + 3], s, rcp, fast);
       const u32x4 lo = u32x4{wd[0], wd[1], wd[2], wd[3]}, hi = u32x4{wd[4], wd[5], wd[6], wd[7]};
       uint8_t* la = a_lds + r * a_stride + c * kEPL;
       *reinterpret_cast<u32x4*>(la) = lo;
