@@ -204,3 +204,58 @@ def test_pack_weight_layout(lib, rows, K):
     if prow > rows:
         pad = _unpack(flat, prow, K)[rows:]
         assert not pad.any(), "padding rows must be zero"
+
+
+def _random_shapes(n, seed):
+    """Seeded shapes within the API's rules: M in [1, 700], N a multiple of 8 up to 1,000,
+    K a multiple of 128 up to 1,536; kind and rotation drawn too."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        kind = ("linear", "gateup", "fp8")[i % 3]
+        M = int(rng.integers(1, 701))
+        N = int(rng.integers(1, 126)) * 8
+        K = int(rng.integers(1, 13)) * 128
+        rot = int(rng.integers(0, 2)) * 128
+        out.append(W.custom(kind, M, K, N, rot, bias=bool(rng.integers(0, 2)), seed=100 + i))
+    return out
+
+
+RANDOM = _random_shapes(9, seed=2026)
+
+
+@pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
+def test_random_shapes_every_element(lib, orc, wl):
+    """Seeded random shapes (ragged M, N and K, every path kind, with and without rotation),
+    every element against the oracle through both weight layouts."""
+    _check_workload(lib, orc, wl)
+
+
+def test_concurrent_streams(lib):
+    """Two unrelated whole-path calls running at the same time on two streams, each with
+    its own workspace, give the bytes of the same calls run one after the other (the
+    library keeps no mutable state between calls)."""
+    dev = torch.device("cuda")
+    cases = []
+    for kind, M, K, N, rot, seed in (("linear", 1502, 1024, 1024, 128, 31), ("gateup", 700, 512, 640, 0, 32)):
+        wl = W.custom(kind, M, K, N, rot, seed=seed)
+        inp = W.make_inputs(wl)
+        wq, s_ch = lib.w8a8_quantize_act(inp.w.to(dev), rot)
+        cases.append((wl, inp.x.to(dev), lib.w8a8_pack_weight(wq), s_ch, inp.bias.to(dev)))
+    torch.cuda.synchronize()
+    seq = [_gpu_path_packed(lib, wl, x, wp, s_ch, b) for wl, x, wp, s_ch, b in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = []
+    for _ in range(3):
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
+        res = [None, None]
+        for i, ((wl, x, wp, s_ch, b), st) in enumerate(zip(cases, streams)):
+            with torch.cuda.stream(st):
+                res[i] = _gpu_path_packed(lib, wl, x, wp, s_ch, b)
+        torch.cuda.synchronize()
+        outs.append(res)
+    for res in outs:
+        for got, ref in zip(res, seq):
+            assert torch.equal(got, ref), "concurrent calls differ from sequential ones"
