@@ -9,7 +9,11 @@
 //             card, Benefits list);
 //   kSwiglu : bf16(silu(g) * u) with g, u the dequantized values of packed rows
 //             n and N + n -- the paired gate/up epilogue ("Loading CLEF INT8",
-//             fuse_mlp; gate/up packed into one weight at load time).
+//             fuse_mlp; gate/up packed into one weight at load time);
+//   kSwigluQ: that SwiGLU output quantized for the next linear, first step:
+//             int8 codes of each 128-column block on the block's own scale
+//             plus the block amax (requant.hip rescales them to the row scale).
+// The bf16 outputs go through LDS so that stores cover whole row segments.
 //
 // Design.  Both operands are K-contiguous ("NT"), so MFMA operands load with no
 // transpose.  A workgroup of WGM x WGN waves owns a BM (tokens) x BN (weight
@@ -51,7 +55,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // staging (HIP's uint4 is a union
                                                               // struct that defeats SROA)
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
@@ -410,9 +413,9 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
       b_off[i] = src_off(min<int64_t>(r, N - 1 - nb), c, PB);
     }
   }
-  // Stages past the last one re-load the last stage into a buffer nobody reads
-  // again, so every stage issues the same number of loads (constant vmcnt
-  // accounting, no branches in the loop body).
+  // Stages past the last one re-load the last stage (their fragments, read by
+  // the last stage, are never multiplied), so every stage issues the same
+  // number of loads (constant vmcnt accounting, no branches in the loop body).
   const int64_t ksteps = K / BK;
   auto issue = [&](int64_t step) __attribute__((always_inline)) {
     // 32-bit per-stage offsets off a uniform panel base: the loads use the

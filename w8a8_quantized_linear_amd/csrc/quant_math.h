@@ -1,5 +1,6 @@
 // Device-side arithmetic of the per-row quantizer, shared by the quantizer
-// kernel and the single-launch short-input path (no state; header-only).
+// kernel, the single-launch short-input path and the GEMM epilogue that
+// quantizes the SwiGLU output (no state; header-only).
 //
 // The rotation, scale and code rules follow the per-token activation quantizer
 // of the ConvRot INT8 path ("CLEF Calibrated INT8 ConvRot" card, notes under the
