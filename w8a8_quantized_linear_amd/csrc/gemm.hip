@@ -239,12 +239,11 @@ __device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], cons
     for (int j = 0; j < qm::kEPL; ++j) a = fmaxf(a, fabsf(y[j]));
     a = fmaxf(a, __shfl_xor(a, 1, 64));
     a = fmaxf(a, __shfl_xor(a, 2, 64));
-    const float s = a / 127.0f;  // IEEE division
-    const float r = a > 0.0f ? 1.0f / s : 0.0f;  // a zero block: r = 0 gives zero codes
-    const bool fast = qm::fast_quotient_ok(s);
+    const qm::QuotientScale qs = qm::quotient_scale(a / 127.0f);  // IEEE division; a zero block gives zero codes
+    qm::apply_prefactor(y, qs);
     uint32_t w[8];
 #pragma unroll
-    for (int g = 0; g < 8; ++g) w[g] = qm::int8_codes4(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3], s, r, fast);
+    for (int g = 0; g < 8; ++g) w[g] = qm::int8_codes4(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3], qs.s, qs.r);
     const int64_t c0 = nb + 32 * p;  // first column of this lane's 32
     if (c0 < N) {
       uint8_t* dst = qo.codes + ((m / 32) * kblocks + c0 / 64) * 2048 + (m % 32) * 64 + (c0 % 64);

@@ -41,40 +41,64 @@ __device__ __forceinline__ double quad_xor(double v) {
   return __longlong_as_double(((long long)hi << 32) | (unsigned)lo);
 }
 
-// int8 codes.  The code of y is round-half-even(fl32(y / s)) (|y| <= amax, so
-// |y / s| <= 127 * (1 + 2^-23) and no clamp is ever needed).  With
-// r = fl32(1/s) correctly rounded, t = fl32(y * r) lies within one ulp of y / s,
-// so e = y - t * s is exact in one FMA and fl32(t + e * r) is the correctly
-// rounded quotient (Markstein's theorem for a correctly rounded reciprocal;
-// also checked against the IEEE division on 1.7e10 random and near-tie pairs,
-// no difference).  This needs the residual e in the normal range wherever the
-// rounding can matter (|y / s| >= 1/2): s >= 2^-100 is enough; smaller scales
-// take the IEEE division.  Adding 1.5 * 2^23 to the quotient rounds it to an
-// integer, half to even, in the low bits of its representation, whose low
-// byte is the two's-complement code.
+// Exact quotients.  Both code rules start from fl32(y / s): int8 rounds it half
+// to even (|y| <= amax, so |y / s| <= 127 * (1 + 2^-23) and no clamp is ever
+// needed), E4M3FN clamps it to +-448 and converts it.  With r = fl32(1/s)
+// correctly rounded, t = fl32(y * r) lies within one ulp of y / s, so the
+// residual e = y - t * s is exact in one FMA and fl32(t + e * r) is the
+// correctly rounded quotient (Markstein's theorem for a correctly rounded
+// reciprocal; also checked against the IEEE division on 1.7e10 random and
+// near-tie pairs, no difference).  The residual is exact as long as
+// exponent(t) + exponent(s) >= -103; the codes depend on the quotient only where
+// |y / s| >= 2^-10 (E4M3FN's smallest rounding boundary; int8's is 1/2), so a
+// scale of at least 2^-90 is enough.  A row with a smaller (nonzero) scale is
+// first multiplied, values and scale alike, by 2^64: exact both ways
+// (s >= 2^-149 lands at >= 2^-85, |y| <= 448 s stays far below overflow, and a
+// power-of-two product of a subnormal loses no bits), and the real quotient is
+// unchanged, so the codes are too.  For int8, adding 1.5 * 2^23 to the quotient
+// rounds it to an integer, half to even, in the low bits of its
+// representation, whose low byte is the two's-complement code.
 constexpr float kRoundMagic = 12582912.0f;  // 1.5 * 2^23
+constexpr float kTinyScale = 0x1p-90f;      // below this the row is rescaled
+constexpr float kRescale = 0x1p64f;
 
-// True when the fast exact quotient applies to this scale (s = 0, with r = 0,
-// gives zero codes).
-__device__ __forceinline__ bool fast_quotient_ok(float s) { return s >= 0x1p-100f || s == 0.0f; }
+// Scale and reciprocal the quotients of a row are formed with, and the factor
+// its values must be multiplied by first (1, or 2^64 for a scale below 2^-90; a
+// zero scale gives r = 0 and zero quotients).
+struct QuotientScale {
+  float s, r, pre;
+};
+__device__ __forceinline__ QuotientScale quotient_scale(float s) {
+  const bool tiny = s < kTinyScale && s > 0.0f;
+  const float sq = tiny ? s * kRescale : s;
+  return QuotientScale{sq, s > 0.0f ? 1.0f / sq : 0.0f, tiny ? kRescale : 1.0f};
+}
 
-// Low byte = code of y (the result's bits; see above).
-__device__ __forceinline__ uint32_t code_bits(float y, float s, float r, bool fast) {
-  float q;
-  if (fast) {
-    const float t = y * r;
-    q = __builtin_fmaf(__builtin_fmaf(-t, s, y), r, t);
-  } else {
-    q = y / s;  // IEEE division (uniform per row; never taken for realistic scales)
+// Multiplies a lane's values by the row's pre-factor: one branch per lane,
+// skipped by the whole wave unless one of its rows has a scale below 2^-90.
+template <int N>
+__device__ __forceinline__ void apply_prefactor(float (&v)[N], const QuotientScale& q) {
+  if (q.pre != 1.0f) {
+#pragma unroll
+    for (int j = 0; j < N; ++j) v[j] *= q.pre;
   }
-  return __float_as_uint(q + kRoundMagic);
+}
+
+// fl32(y / s) for y carrying the row's pre-factor (see above).
+__device__ __forceinline__ float quotient(float y, float s, float r) {
+  const float t = y * r;
+  return __builtin_fmaf(__builtin_fmaf(-t, s, y), r, t);
+}
+
+// Low byte = int8 code of y.
+__device__ __forceinline__ uint32_t code_bits(float y, float s, float r) {
+  return __float_as_uint(quotient(y, s, r) + kRoundMagic);
 }
 
 // Four codes packed as int8 bytes (byte i = code of y_i).
-__device__ __forceinline__ uint32_t int8_codes4(float y0, float y1, float y2, float y3, float s, float r,
-                                               bool fast) {
-  const uint32_t u0 = code_bits(y0, s, r, fast), u1 = code_bits(y1, s, r, fast);
-  const uint32_t u2 = code_bits(y2, s, r, fast), u3 = code_bits(y3, s, r, fast);
+__device__ __forceinline__ uint32_t int8_codes4(float y0, float y1, float y2, float y3, float s, float r) {
+  const uint32_t u0 = code_bits(y0, s, r), u1 = code_bits(y1, s, r);
+  const uint32_t u2 = code_bits(y2, s, r), u3 = code_bits(y3, s, r);
   // v_perm_b32 selectors: 0..3 pick bytes of the second operand, 4..7 of the
   // first, 0x0c gives 0x00
   const uint32_t lo = __builtin_amdgcn_perm(u1, u0, 0x0c0c0400u);  // [u0.b0, u1.b0, 0, 0]

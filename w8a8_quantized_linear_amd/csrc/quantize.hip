@@ -22,11 +22,11 @@
 //     fl64(2^-3.5) and rounded once to fp32.  The codes are therefore those of
 //     the exactly rotated row.
 //   * amax by wave butterfly plus an LDS step across the row's waves.
-//   * int8 codes: the exact quotient fl32(y / s) from r = fl32(1/s) with one
-//     multiply and two FMAs (a correctly rounded reciprocal makes one
-//     correction step exact), rounded half to even by adding 1.5 * 2^23; no
-//     branch, no clamp (quant_math.h states the argument).  E4M3FN codes use the IEEE division and the hardware RNE
-//     converter after clamping to +-448.
+//   * Codes from the exact quotient fl32(y / s), formed from r = fl32(1/s)
+//     with one multiply and two FMAs (a correctly rounded reciprocal makes one
+//     correction step exact; quant_math.h states the argument): int8 rounds it
+//     half to even by adding 1.5 * 2^23 (no branch, no clamp), E4M3FN clamps
+//     it to +-448 and takes the hardware RNE converter.
 //   * Code stores, row-major or in the GEMM's packed layout (blocks of 32 rows
 //     x 64 bytes, block (r / 32, k / 64) at byte ((r / 32) * (K / 64) + k / 64)
 //     * 2048): with rotation a lane's 32 contiguous codes go out as two
@@ -125,9 +125,10 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
   const float s = amax / kQmax;  // IEEE division
   if (!live) return;
   if (tid == 0) s_out[row] = s;
-  const bool zero_row = !(amax > 0.0f);
-  const float r = zero_row ? 0.0f : 1.0f / s;
-  const bool fast = fast_quotient_ok(s);
+  const QuotientScale qs = quotient_scale(s);
+  const uint32_t zero_mask = s > 0.0f ? ~0u : 0u;
+#pragma unroll
+  for (int i = 0; i < CMAX; ++i) apply_prefactor(y[i], qs);
 
   // element e of this row (e % 8 == 0) goes to qr + (e & ~63) * kstride + (e & 63)
   uint8_t* qr = q + (packed ? (row / 32) * 32 * (int64_t)K + (row % 32) * 64 : row * (int64_t)K);
@@ -141,15 +142,16 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
       if constexpr (FP8) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          t[e] = zero_row ? 0.0f : y[i][8 * v + 4 * g + e] / s;
-          t[e] = fminf(fmaxf(t[e], -448.0f), 448.0f);
+          // (the correction step turns y = -0 into +0; the quotient takes y's sign)
+          const float yv = y[i][8 * v + 4 * g + e];
+          t[e] = fminf(fmaxf(__builtin_copysignf(quotient(yv, qs.s, qs.r), yv), -448.0f), 448.0f);
         }
         int wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[0], t[1], 0, false);
         wd = __builtin_amdgcn_cvt_pk_fp8_f32(t[2], t[3], wd, true);
-        out[g] = (uint32_t)wd;
+        out[g] = (uint32_t)wd & zero_mask;  // a zero row's codes are +0
       } else {
         const float* yg = &y[i][8 * v + 4 * g];
-        out[g] = int8_codes4(yg[0], yg[1], yg[2], yg[3], s, r, fast);  // (r = 0 for a zero row: zero codes)
+        out[g] = int8_codes4(yg[0], yg[1], yg[2], yg[3], qs.s, qs.r);  // (r = 0 for a zero row: zero codes)
       }
     }
   };

@@ -148,9 +148,9 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
 #pragma unroll
     for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
     const float s = amax / 127.0f;             // IEEE division
-    const bool zero_row = !(amax > 0.0f);
-    const float rcp = zero_row ? 0.0f : 1.0f / s;
-    const bool fast = fast_quotient_ok(s);
+    const QuotientScale qs = quotient_scale(s);
+#pragma unroll
+    for (int i = 0; i < kCPL; ++i) apply_prefactor(v[i], qs);
     const bool write_ws = tile_n == 0 && live;
     if (q == 0) {
       s_rows[r] = s;
@@ -164,7 +164,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
       uint32_t wd[8];
 #pragma unroll
       for (int g = 0; g < 8; ++g)
-        wd[g] = int8_codes4(v[i][4 * g], v[i][4 * g + 1], v[i][4 * g + 2], v[i][4 * g + 3], s, rcp, fast);
+        wd[g] = int8_codes4(v[i][4 * g], v[i][4 * g + 1], v[i][4 * g + 2], v[i][4 * g + 3], qs.s, qs.r);
       const u32x4 lo = u32x4{wd[0], wd[1], wd[2], wd[3]}, hi = u32x4{wd[4], wd[5], wd[6], wd[7]};
       uint8_t* la = a_lds + r * a_stride + c * kEPL;
       *reinterpret_cast<u32x4*>(la) = lo;
