@@ -11,18 +11,24 @@
 // round trip of the codes through memory cost more than the arithmetic.
 //
 // Design.  A workgroup owns 32 token rows and 64 weight rows (64 output
-// columns, or 32 gate + 32 up rows) and runs three phases:
-//   0. every wave issues the direct-to-LDS loads of all its weight stages
-//      (a quarter of K, 32 bytes per stage, its own LDS region), so they land
-//      while the rows are quantized;
-//   1. it quantizes its own 32 rows into LDS (8 lanes per row, each holding up
-//      to 4 chunks of 32 rotated values in registers: one pass over the row),
-//      and the workgroups of the first weight tile also write the codes (packed
-//      layout) and scales to the workspace;
-//   2. each of the 4 waves multiplies its quarter of K from LDS, with no
-//      barriers;
-//   3. the int32 partial sums of waves 1..3 are added to wave 0's through LDS
-//      (exact) and wave 0 runs the usual epilogue.
+// columns, or 32 gate + 32 up rows); 4 waves, each multiplying one quarter of
+// K.  The critical path is the row loads, then the quantization (vector ALU
+// bound: every tile quantizes its rows again), then a short MFMA phase and the
+// epilogue, so everything else is issued early and kept off that path:
+//   0. every lane issues the loads of its share of the 32 rows, then the MFMA
+//      fragments of its wave's weights (each weight byte of the tile feeds
+//      exactly one lane, so the fragments go straight to registers: no LDS
+//      staging), then the channel scales and bias of the outputs it will
+//      write.  All loads are unconditional register loads, so the compiler's
+//      waits drain them in order, piece by piece;
+//   1. the rows are quantized into LDS (8 lanes per row; without rotation each
+//      load instruction reads one contiguous 128-byte piece per row, with it a
+//      lane holds 32 consecutive elements of a 128-block);
+//   2. each wave multiplies its quarter of K (token codes from LDS, weights
+//      from registers), while the workgroups of the first weight tile write
+//      the codes (packed layout) and scales to the workspace;
+//   3. the int32 partial sums of the 4 waves meet in LDS (exact) and every
+//      thread finishes 8 (SwiGLU: 4) outputs of one row with one store.
 // Every tile quantizes its rows again; this is meant for batches whose whole
 // quantization costs less than a kernel launch.
 #include <type_traits>
@@ -41,22 +47,8 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kBM = 32, kBW = 64;        // token rows, weight rows per tile
 constexpr int kMaxK = 1024;
-constexpr int kStages = kMaxK / 4 / 32;  // weight stages per wave (all resident)
-constexpr int kStageB = kBW * 32;        // 64 rows x 32 bytes of K
+constexpr int kSteps = kMaxK / 4 / 32;   // 32-deep MFMA steps per wave (a quarter of K)
 constexpr int kCPL = kMaxK / kEPL / 8;   // chunks of 32 elements per lane (8 lanes per row)
-
-__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* l) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-#endif
-}
-
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
-}
-
 
 template <Epi EPI, bool ROT, bool PB>
 __global__ void __launch_bounds__(256)
@@ -64,203 +56,229 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
              const float* __restrict__ s_ch, const uint16_t* __restrict__ bias,
              uint16_t* __restrict__ y, int64_t M, int64_t N, int K, uint8_t* __restrict__ q_ws,
              float* __restrict__ s_ws, int tiles_n) {
+  constexpr bool SWIGLU = EPI == Epi::kSwiglu;
   constexpr int A_BYTES = kBM * (kMaxK + 16);
-  constexpr int B_BYTES = 4 * kStages * kStageB;
-  static_assert(3 * 2 * 16 * 64 * 4 <= B_BYTES, "partial sums fit in the weight stages");
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[A_BYTES + B_BYTES];
+  // partial sums after the MFMA phase, over the codes:
+  // [wave][block t][qq][half h][token row j] x 16 bytes (4 int32)
+  constexpr int RED_BYTES = 4 * 2 * 4 * 2 * 32 * 16;
+  static_assert(RED_BYTES <= A_BYTES, "partial sums fit over the codes");
+  __shared__ __attribute__((aligned(1024))) uint8_t a_lds[A_BYTES];
   __shared__ float s_rows[kBM];
   const int a_stride = K + 16;                 // 16-byte skew per row: conflict-free fragment reads
-  uint8_t* a_lds = lds;
-  uint8_t* b_lds = lds + A_BYTES;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tile_m = blockIdx.x / tiles_n, tile_n = blockIdx.x % tiles_n;
   const int64_t mb = (int64_t)tile_m * kBM;
-  const int64_t nb = (EPI == Epi::kSwiglu) ? (int64_t)tile_n * (kBW / 2) : (int64_t)tile_n * kBW;
+  const int64_t nb = SWIGLU ? (int64_t)tile_n * (kBW / 2) : (int64_t)tile_n * kBW;
 
-  // ---- phase 0: wave `wave` loads its weight rows for K range [wave * K/4, (wave + 1) * K/4) ----
-  // Weight stage: 64 rows x 32 bytes in LDS, row r at 32r, its two 16-byte
-  // chunks swapped for rows with bit 2 set (conflict-free fragment reads).
-  // One load instruction covers 32 rows: lane -> slot p = 64 i + lane, row p / 2.
+  // ---- phase 0a: loads of this lane's share of row mb + r --------------------
+  // 8 lanes per row.  Piece i*4+p of lane q (8 bf16 values, 16 bytes):
+  //   rotation: chunk c = 8i + q (32 elements, a quarter of a 128-block; the 4
+  //             lanes of a DPP quad hold one block), elements 32c + 8p ..;
+  //   none:     elements 64 (4i + p) + 8q .. (the row's 8 lanes read 128
+  //             contiguous bytes per instruction).
+  // Pieces past K (K < 1024) read the same position of the row's first
+  // 128-block instead: real values of the row, so the amax is unchanged (with
+  // rotation the quad rotates block 0 again), and their codes are never stored.
+  const int r = tid >> 3, q = tid & 7;
+  const int64_t m = mb + r;
+  const bool live = m < M;
+  const uint16_t* xr = x + (live ? m : M - 1) * (int64_t)K;
+  auto elem = [&](int i, int p) -> int {
+    if constexpr (ROT) return (8 * i + q) * kEPL + 8 * p;
+    else return 64 * (4 * i + p) + 8 * q;
+  };
+  u32x4 raw[kCPL][4];
+#pragma unroll
+  for (int i = 0; i < kCPL; ++i)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int e = elem(i, p);
+      raw[i][p] = *reinterpret_cast<const u32x4*>(xr + (e < K ? e : e & 127));
+    }
+
+  // ---- phase 0b: this lane's weight fragments for the wave's quarter of K ----
+  // MFMA 32x32x32 operand: lane (row rr % 32 = lane % 32, half = lane / 32)
+  // holds bytes 16 half .. 16 half + 15 of a 32-byte step of weight row rr,
+  // for the two 32-row blocks t (rows 32 t + lane % 32 of the tile).  Steps
+  // past K / 128 repeat the last one (never multiplied).
+  const int frag_row = lane & 31, frag_half = lane >> 5;
   const int kq = K / 4, steps = kq / 32;
-  const int64_t k_begin = (int64_t)wave * kq;
-  // (b_base is per lane: the up rows of a gate/up tile need not start on a
-  // 32-row boundary, so the loads use the 64-bit vector address form)
-  uint32_t b_off[2];
-  const uint8_t* b_base[2];
+  const int k_begin = wave * kq;
+  v4i fb[kSteps][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int p = 64 * i + lane, r = p / 2, c = (p & 1) ^ ((r >> 2) & 1);
+  for (int t = 0; t < 2; ++t) {
     int64_t row;                               // absolute weight row (clamped: unused rows re-read the last)
-    if constexpr (EPI == Epi::kSwiglu) {
-      const int64_t col = min<int64_t>(nb + (r % 32), N - 1);
-      row = r < 32 ? col : N + col;
+    if constexpr (SWIGLU) {
+      const int64_t col = min<int64_t>(nb + frag_row, N - 1);
+      row = t == 0 ? col : N + col;
     } else {
-      row = min<int64_t>(nb + r, N - 1);
+      row = min<int64_t>(nb + 32 * t + frag_row, N - 1);
     }
-    // relative to a 32-row-aligned base so the per-lane offset stays small
-    const int64_t base_row = row / 32 * 32;
-    b_base[i] = w + base_row * K;
-    const int64_t rel = row - base_row;
-    b_off[i] = PB ? (uint32_t)(rel * 64 + c * 16) : (uint32_t)(rel * K + c * 16);
-  }
-  uint8_t* ring = b_lds + wave * (kStages * kStageB);
-  // stage st of this wave -> its own LDS slot st (steps <= kStages)
-  for (int st = 0; st < steps; ++st) {
-    const int64_t k = k_begin + (int64_t)st * 32;
-    const uint32_t koff = PB ? (uint32_t)((k / 64) * 2048 + (k % 64)) : (uint32_t)k;
-    uint8_t* dst = ring + st * kStageB;
+    const uint8_t* wr = PB ? w + (row / 32) * 32 * (int64_t)K + (row % 32) * 64 : w + row * (int64_t)K;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(b_base[i] + (b_off[i] + koff), dst + i * 1024);
+    for (int st = 0; st < kSteps; ++st) {
+      const int k = k_begin + 32 * min(st, steps - 1) + 16 * frag_half;
+      fb[st][t] = *reinterpret_cast<const v4i*>(wr + (PB ? (k / 64) * 2048 + (k % 64) : k));
+    }
   }
+
+  // ---- phase 0c: channel scales and bias of this thread's outputs ----------
+  // Output role: token row er = tid % 32, column group ec = tid / 32 -- 8
+  // columns nb + 8 ec .. (SwiGLU: 4 columns nb + 4 ec .., gate and up).
+  const int er = tid & 31, ec = tid >> 5;
+  constexpr int kOutCols = SWIGLU ? 4 : 8;
+  const int64_t n0 = nb + (int64_t)kOutCols * ec;
+  const bool col_live = n0 < N;                // N % 8 == 0: the group is whole or absent
+  // dequant: columns n0 .. n0+3 and n0+4 .. n0+7; SwiGLU: gate n0 .., up N + n0 ..
+  // (a thread past N reads column 0; kept raw until the epilogue)
+  const int64_t c0 = col_live ? n0 : 0, c1 = SWIGLU ? N + c0 : c0 + 4;
+  const float4 sc0 = *reinterpret_cast<const float4*>(s_ch + c0);
+  const float4 sc1 = *reinterpret_cast<const float4*>(s_ch + c1);
+  // (no bias: the same offsets of s_ch, which is at least as long, are read and
+  // ignored; a conditional load would make the compiler drain every load)
+  const uint16_t* bsrc = bias ? bias : reinterpret_cast<const uint16_t*>(s_ch);
+  const uint2 bw0 = *reinterpret_cast<const uint2*>(bsrc + c0);
+  const uint2 bw1 = *reinterpret_cast<const uint2*>(bsrc + c1);
+  // (keeps the compiler from sinking the weight loads below the quantization)
+  __builtin_amdgcn_sched_barrier(0);
+
   // ---- phase 1: quantize rows mb .. mb+31 into LDS --------------------------
-  {
-    const int r = tid >> 3, q = tid & 7;       // 8 lanes per row; lanes 4q'..4q'+3 form DPP quads
-    const int64_t m = mb + r;
-    const bool live = m < M;
-    const uint16_t* xr = x + (live ? m : M - 1) * (int64_t)K;
-    const int nchunks = K / kEPL;              // chunk c = 8 i + q of the row is this lane's chunk i
-    u32x4 raw[kCPL][4];
+  float v[kCPL][kEPL];
+  float amax = 0.0f;
 #pragma unroll
-    for (int i = 0; i < kCPL; ++i) {
-      const int c = 8 * i + q;
+  for (int i = 0; i < kCPL; ++i) {
+    if constexpr (ROT) {
+      rotate_chunk(raw[i], lane, v[i]);
+    } else {
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
-        raw[i][p] = c < nchunks ? *reinterpret_cast<const u32x4*>(xr + c * kEPL + 8 * p) : u32x4{0, 0, 0, 0};
-    }
-    float v[kCPL][kEPL];
-    float amax = 0.0f;
-#pragma unroll
-    for (int i = 0; i < kCPL; ++i) {
-      if constexpr (ROT) {
-        rotate_chunk(raw[i], lane, v[i]);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) {
-          const uint32_t wd = raw[i][j / 4][j % 4];
-          v[i][2 * j] = bf16lo(wd);
-          v[i][2 * j + 1] = bf16hi(wd);
-        }
+      for (int j = 0; j < 16; ++j) {
+        const uint32_t wd = raw[i][j / 4][j % 4];
+        v[i][2 * j] = bf16lo(wd);
+        v[i][2 * j + 1] = bf16hi(wd);
       }
-#pragma unroll
-      for (int j = 0; j < kEPL; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
     }
 #pragma unroll
-    for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
-    const float s = amax / 127.0f;             // IEEE division
-    const QuotientScale qs = quotient_scale(s);
+    for (int j = 0; j < kEPL; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
+  }
 #pragma unroll
-    for (int i = 0; i < kCPL; ++i) apply_prefactor(v[i], qs);
-    const bool write_ws = tile_n == 0 && live;
-    if (q == 0) {
-      s_rows[r] = s;
-      if (write_ws) s_ws[m] = s;
+  for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  const float s = amax / 127.0f;               // IEEE division
+  const QuotientScale qs = quotient_scale(s);
+#pragma unroll
+  for (int i = 0; i < kCPL; ++i) apply_prefactor(v[i], qs);
+  if (q == 0) s_rows[r] = s;
+  // codes of piece i*4+p: words cw[i][2p], cw[i][2p+1]
+  uint32_t cw[kCPL][8];
+#pragma unroll
+  for (int i = 0; i < kCPL; ++i)
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+      cw[i][g] = int8_codes4(v[i][4 * g], v[i][4 * g + 1], v[i][4 * g + 2], v[i][4 * g + 3], qs.s, qs.r);
+#pragma unroll
+  for (int i = 0; i < kCPL; ++i) {
+    if constexpr (ROT) {
+      const int e = elem(i, 0);
+      if (e >= K) continue;
+      uint8_t* la = a_lds + r * a_stride + e;
+      *reinterpret_cast<u32x4*>(la) = u32x4{cw[i][0], cw[i][1], cw[i][2], cw[i][3]};
+      *reinterpret_cast<u32x4*>(la + 16) = u32x4{cw[i][4], cw[i][5], cw[i][6], cw[i][7]};
+    } else {
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const int e = elem(i, p);
+        if (e >= K) continue;
+        *reinterpret_cast<u32x2*>(a_lds + r * a_stride + e) = u32x2{cw[i][2 * p], cw[i][2 * p + 1]};
+      }
     }
+  }
+  __syncthreads();                             // every row's codes are in LDS
+
+  // ---- workspace: codes (packed layout) and scales, first weight tile only ----
+  if (tile_n == 0 && live) {
+    if (q == 0) s_ws[m] = s;
     uint8_t* qg = q_ws + (m / 32) * 32 * (int64_t)K + (m % 32) * 64;   // packed row m
 #pragma unroll
     for (int i = 0; i < kCPL; ++i) {
-      const int c = 8 * i + q;
-      if (c >= nchunks) continue;
-      uint32_t wd[8];
+      if constexpr (ROT) {
+        const int e = elem(i, 0);              // 32 codes inside one 64-byte group
+        if (e >= K) continue;
+        uint8_t* dst = qg + (e / 64) * 2048 + (e % 64);
+        *reinterpret_cast<u32x4*>(dst) = u32x4{cw[i][0], cw[i][1], cw[i][2], cw[i][3]};
+        *reinterpret_cast<u32x4*>(dst + 16) = u32x4{cw[i][4], cw[i][5], cw[i][6], cw[i][7]};
+      } else {
 #pragma unroll
-      for (int g = 0; g < 8; ++g)
-        wd[g] = int8_codes4(v[i][4 * g], v[i][4 * g + 1], v[i][4 * g + 2], v[i][4 * g + 3], qs.s, qs.r);
-      const u32x4 lo = u32x4{wd[0], wd[1], wd[2], wd[3]}, hi = u32x4{wd[4], wd[5], wd[6], wd[7]};
-      uint8_t* la = a_lds + r * a_stride + c * kEPL;
-      *reinterpret_cast<u32x4*>(la) = lo;
-      *reinterpret_cast<u32x4*>(la + 16) = hi;
-      if (write_ws) {
-        const int k = c * kEPL;                // 32 codes inside one 64-byte group
-        uint8_t* dst = qg + (k / 64) * 2048 + (k % 64);
-        *reinterpret_cast<u32x4*>(dst) = lo;
-        *reinterpret_cast<u32x4*>(dst + 16) = hi;
+        for (int p = 0; p < 4; ++p) {
+          const int e = elem(i, p);            // 8 codes inside one 64-byte group
+          if (e >= K) continue;
+          *reinterpret_cast<u32x2*>(qg + (e / 64) * 2048 + (e % 64)) = u32x2{cw[i][2 * p], cw[i][2 * p + 1]};
+        }
       }
     }
   }
-  // every wave's weight stages have landed (its own loads), and everyone's codes
-  wait_vm<0>();
-  __syncthreads();
 
-  // ---- phase 2: multiply this wave's quarter of K from LDS -------------------
+  // ---- phase 2: multiply this wave's quarter of K ----------------------------
   v16i acc[2] = {v16i{}, v16i{}};
-  const int frag_row = lane & 31, frag_half = lane >> 5;
-  for (int s = 0; s < steps; ++s) {
-    const uint8_t* bs = ring + s * kStageB;
-    const int k = (int)(k_begin + s * 32) + 16 * frag_half;
+#pragma unroll
+  for (int st = 0; st < kSteps; ++st) {
+    if (st >= steps) break;                    // uniform
+    const int k = k_begin + 32 * st + 16 * frag_half;
     const v4i fa = *reinterpret_cast<const v4i*>(a_lds + frag_row * a_stride + k);
-    v4i fb[2];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r = 32 * t + frag_row, c = frag_half ^ ((r >> 2) & 1);
-      fb[t] = *reinterpret_cast<const v4i*>(bs + r * 32 + c * 16);
-    }
-#pragma unroll
-    for (int t = 0; t < 2; ++t) acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[t], fa, acc[t], 0, 0, 0);
+    for (int t = 0; t < 2; ++t) acc[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[st][t], fa, acc[t], 0, 0, 0);
   }
-  __syncthreads();
+  __syncthreads();                             // every wave is done with the codes
 
-  // ---- phase 3: add the partial sums, epilogue ------------------------------
-  int32_t* red = reinterpret_cast<int32_t*>(b_lds);
-  if (wave > 0) {
+  // ---- phase 3: partial sums through LDS, epilogue ---------------------------
+  // 32x32 block layout: lane (j = lane % 32, h = lane / 32) holds token row j,
+  // weight rows 8 qq + 4 h + 0..3 of block t in acc[t][4 qq .. 4 qq + 3].
+  v4i* red = reinterpret_cast<v4i*>(a_lds);
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) red[(((wave - 1) * 2 + t) * 16 + v) * 64 + lane] = acc[t][v];
+    for (int qq = 0; qq < 4; ++qq)
+      red[(((wave * 2 + t) * 4 + qq) * 2 + frag_half) * 32 + frag_row] =
+          v4i{acc[t][4 * qq], acc[t][4 * qq + 1], acc[t][4 * qq + 2], acc[t][4 * qq + 3]};
+  __syncthreads();
+  // this thread's 8 sums: dequant -> block t = ec / 4, rows 8 (ec % 4) + 0..7
+  // (halves 0 and 1); SwiGLU -> rows 4 ec + 0..3 (qq = ec / 2, h = ec % 2) of
+  // the gate block (t = 0) and of the up block (t = 1)
+  const int t0 = SWIGLU ? 0 : ec / 4, t1 = SWIGLU ? 1 : ec / 4;
+  const int qq = SWIGLU ? ec / 2 : ec % 4, h0 = SWIGLU ? ec % 2 : 0, h1 = SWIGLU ? ec % 2 : 1;
+  v4i s0 = v4i{0, 0, 0, 0}, s1 = v4i{0, 0, 0, 0};
+#pragma unroll
+  for (int wv = 0; wv < 4; ++wv) {
+    s0 += red[(((wv * 2 + t0) * 4 + qq) * 2 + h0) * 32 + er];
+    s1 += red[(((wv * 2 + t1) * 4 + qq) * 2 + h1) * 32 + er];
   }
-  __syncthreads();
-  if (wave > 0) return;
+  const int64_t me = mb + er;
+  if (me >= M || !col_live) return;
+  const float st = s_rows[er];
+  const float sc[8] = {sc0.x, sc0.y, sc0.z, sc0.w, sc1.x, sc1.y, sc1.z, sc1.w};
+  float bv[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  if (bias) {
+    bf16x4(bw0, bv);
+    bf16x4(bw1, bv + 4);
+  }
+  const int32_t sums[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
+  uint16_t* yrow = y + me * N + n0;
+  if constexpr (!SWIGLU) {
+    uint16_t o[8];
 #pragma unroll
-  for (int src = 0; src < 3; ++src)
+    for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne(__builtin_fmaf((float)sums[e], st * sc[e], bv[e]));
+    *reinterpret_cast<u32x4*>(yrow) =
+        u32x4{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16),
+              (uint32_t)o[4] | ((uint32_t)o[5] << 16), (uint32_t)o[6] | ((uint32_t)o[7] << 16)};
+  } else {
+    uint16_t o[4];
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[t][v] += red[((src * 2 + t) * 16 + v) * 64 + lane];
-
-  // 32x32 block layout: lane holds token row frag_row, weight rows 8q + 4 h + 0..3
-  const int64_t m = mb + frag_row;
-  if (m >= M) return;
-  const float st = s_rows[frag_row];
-  uint16_t* yrow = y + m * N;
-  if constexpr (EPI == Epi::kDequant) {
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int64_t n0 = nb + t * 32 + 8 * q + 4 * frag_half;
-        if (n0 >= N) continue;
-        const float4 sc = *reinterpret_cast<const float4*>(s_ch + n0);
-        float bv[4] = {0.f, 0.f, 0.f, 0.f};
-        if (bias) bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bv);
-        const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
-        uint16_t o[4];
-#pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_rne(__builtin_fmaf((float)acc[t][4 * q + v], st * scv[v], bv[v]));
-        *reinterpret_cast<uint2*>(yrow + n0) =
-            make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
-      }
-  } else {  // SwiGLU: block 0 holds gate rows, block 1 the matching up rows
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n0 = nb + 8 * q + 4 * frag_half;
-      if (n0 >= N) continue;
-      const float4 sg = *reinterpret_cast<const float4*>(s_ch + n0);
-      const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n0);
-      float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-      if (bias) {
-        bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bg);
-        bf16x4(*reinterpret_cast<const uint2*>(bias + N + n0), bu);
-      }
-      const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
-      uint16_t o[4];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float g = __builtin_fmaf((float)acc[0][4 * q + v], st * sgv[v], bg[v]);
-        const float u = __builtin_fmaf((float)acc[1][4 * q + v], st * suv[v], bu[v]);
-        o[v] = f32_to_bf16_rne(silu_f32(g) * u);
-      }
-      *reinterpret_cast<uint2*>(yrow + n0) =
-          make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+    for (int e = 0; e < 4; ++e) {
+      const float g = __builtin_fmaf((float)sums[e], st * sc[e], bv[e]);
+      const float u = __builtin_fmaf((float)sums[4 + e], st * sc[4 + e], bv[4 + e]);
+      o[e] = f32_to_bf16_rne(silu_f32(g) * u);
     }
+    *reinterpret_cast<u32x2*>(yrow) =
+        u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
   }
 }
 
