@@ -237,8 +237,7 @@ __device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], cons
     float a = 0.0f;
 #pragma unroll
     for (int j = 0; j < qm::kEPL; ++j) a = fmaxf(a, fabsf(y[j]));
-    a = fmaxf(a, __shfl_xor(a, 1, 64));
-    a = fmaxf(a, __shfl_xor(a, 2, 64));
+    a = qm::group_max<4>(a);
     const qm::QuotientScale qs = qm::quotient_scale(a / 127.0f);  // IEEE division; a zero block gives zero codes
     qm::apply_prefactor(y, qs);
     uint32_t w[8];

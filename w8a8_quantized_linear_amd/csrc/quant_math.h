@@ -30,6 +30,23 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+// Max over aligned groups of 4 (GROUP = 4) or 8 (GROUP = 8) lanes, in
+// registers (DPP moves instead of LDS permutes): quad_perm swaps with the lane
+// whose quad position differs in bit 0, then bit 1; for 8, row_half_mirror then
+// brings lane 7 - i of the group, which holds the other quad's max.
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+template <int GROUP>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(GROUP == 4 || GROUP == 8, "groups of 4 or 8 lanes");
+  v = fmaxf(v, dpp_move<0xB1>(v));     // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_move<0x4E>(v));     // quad_perm [2,3,0,1]
+  if constexpr (GROUP == 8) v = fmaxf(v, dpp_move<0x141>(v));  // row_half_mirror
+  return v;
+}
+
 // fp64 value of the lane whose quad position differs in the bits of MASK (1 or 2).
 template <int MASK>
 __device__ __forceinline__ double quad_xor(double v) {

@@ -17,6 +17,7 @@
 // any store (the codes are rewritten in place), and each wave instruction
 // reads or writes one contiguous kilobyte.
 #include "internal.h"
+#include "quant_math.h"
 
 namespace w8a8 {
 namespace {
@@ -56,9 +57,7 @@ requantize_blocks_kernel(uint8_t* __restrict__ codes, const float* __restrict__ 
   float a = 0.0f;
   if (live)
     for (int b = sub; b < nblk; b += 8) a = fmaxf(a, am[b]);
-  a = fmaxf(a, __shfl_xor(a, 1, 64));
-  a = fmaxf(a, __shfl_xor(a, 2, 64));
-  a = fmaxf(a, __shfl_xor(a, 4, 64));
+  a = qm::group_max<8>(a);
   const float s = a / 127.0f;  // IEEE division
   if (live && group == 0 && sub == 0) s_out[m] = s;
   const int b = group * kBlocksPerGroup + sub;

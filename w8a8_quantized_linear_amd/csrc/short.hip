@@ -15,15 +15,16 @@
 // K.  The critical path is the row loads, then the quantization (vector ALU
 // bound: every tile quantizes its rows again), then a short MFMA phase and the
 // epilogue, so everything else is issued early and kept off that path:
-//   0. every lane issues the loads of its share of the 32 rows, then the MFMA
-//      fragments of its wave's weights (each weight byte of the tile feeds
-//      exactly one lane, so the fragments go straight to registers: no LDS
-//      staging), then the channel scales and bias of the outputs it will
-//      write.  All loads are unconditional register loads, so the compiler's
-//      waits drain them in order, piece by piece;
+//   0. every lane issues the loads of its share of the 32 rows, then the
+//      channel scales and bias of the outputs it will write;
 //   1. the rows are quantized into LDS (8 lanes per row; without rotation each
 //      load instruction reads one contiguous 128-byte piece per row, with it a
-//      lane holds 32 consecutive elements of a 128-block);
+//      lane holds 32 consecutive elements of a 128-block).  The MFMA
+//      fragments of the wave's weights are loaded on the way, half after the
+//      row amax and half after the first codes: each weight byte of the tile
+//      feeds exactly one lane, so the fragments go straight to registers (no
+//      LDS staging).  All loads are unconditional register loads, so the
+//      compiler's waits drain them in order, piece by piece;
 //   2. each wave multiplies its quarter of K (token codes from LDS, weights
 //      from registers), while the workgroups of the first weight tile write
 //      the codes (packed layout) and scales to the workspace;
@@ -97,7 +98,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
       raw[i][p] = *reinterpret_cast<const u32x4*>(xr + (e < K ? e : e & 127));
     }
 
-  // ---- phase 0b: this lane's weight fragments for the wave's quarter of K ----
+  // ---- this lane's weight fragments for the wave's quarter of K (loaded in phase 1) ----
   // MFMA 32x32x32 operand: lane (row rr % 32 = lane % 32, half = lane / 32)
   // holds bytes 16 half .. 16 half + 15 of a 32-byte step of weight row rr,
   // for the two 32-row blocks t (rows 32 t + lane % 32 of the tile).  Steps
@@ -106,6 +107,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
   const int kq = K / 4, steps = kq / 32;
   const int k_begin = wave * kq;
   v4i fb[kSteps][2];
+  const uint8_t* wr[2];
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     int64_t row;                               // absolute weight row (clamped: unused rows re-read the last)
@@ -115,15 +117,19 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
     } else {
       row = min<int64_t>(nb + 32 * t + frag_row, N - 1);
     }
-    const uint8_t* wr = PB ? w + (row / 32) * 32 * (int64_t)K + (row % 32) * 64 : w + row * (int64_t)K;
-#pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      const int k = k_begin + 32 * min(st, steps - 1) + 16 * frag_half;
-      fb[st][t] = *reinterpret_cast<const v4i*>(wr + (PB ? (k / 64) * 2048 + (k % 64) : k));
-    }
+    wr[t] = PB ? w + (row / 32) * 32 * (int64_t)K + (row % 32) * 64 : w + row * (int64_t)K;
   }
+  auto load_steps = [&](int first, int last) __attribute__((always_inline)) {
+#pragma unroll
+    for (int st = first; st < last; ++st)
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int k = k_begin + 32 * min(st, steps - 1) + 16 * frag_half;
+        fb[st][t] = *reinterpret_cast<const v4i*>(wr[t] + (PB ? (k / 64) * 2048 + (k % 64) : k));
+      }
+  };
 
-  // ---- phase 0c: channel scales and bias of this thread's outputs ----------
+  // ---- phase 0b: channel scales and bias of this thread's outputs ----------
   // Output role: token row er = tid % 32, column group ec = tid / 32 -- 8
   // columns nb + 8 ec .. (SwiGLU: 4 columns nb + 4 ec .., gate and up).
   const int er = tid & 31, ec = tid >> 5;
@@ -140,7 +146,6 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
   const uint16_t* bsrc = bias ? bias : reinterpret_cast<const uint16_t*>(s_ch);
   const uint2 bw0 = *reinterpret_cast<const uint2*>(bsrc + c0);
   const uint2 bw1 = *reinterpret_cast<const uint2*>(bsrc + c1);
-  // (keeps the compiler from sinking the weight loads below the quantization)
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- phase 1: quantize rows mb .. mb+31 into LDS --------------------------
@@ -161,8 +166,13 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
 #pragma unroll
     for (int j = 0; j < kEPL; ++j) amax = fmaxf(amax, fabsf(v[i][j]));
   }
-#pragma unroll
-  for (int o = 1; o < 8; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  // first half of the weight fragments: issued once the row pieces have been
+  // read, so that they do not hold up the row loads (the second half follows
+  // the first codes; this split measured fastest)
+  __builtin_amdgcn_sched_barrier(0);
+  load_steps(0, kSteps / 2);
+  __builtin_amdgcn_sched_barrier(0);
+  amax = group_max<8>(amax);                   // the row's 8 lanes
   const float s = amax / 127.0f;               // IEEE division
   const QuotientScale qs = quotient_scale(s);
 #pragma unroll
@@ -171,10 +181,17 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
   // codes of piece i*4+p: words cw[i][2p], cw[i][2p+1]
   uint32_t cw[kCPL][8];
 #pragma unroll
-  for (int i = 0; i < kCPL; ++i)
+  for (int i = 0; i < kCPL; ++i) {
 #pragma unroll
     for (int g = 0; g < 8; ++g)
       cw[i][g] = int8_codes4(v[i][4 * g], v[i][4 * g + 1], v[i][4 * g + 2], v[i][4 * g + 3], qs.s, qs.r);
+    if (i == 0) {
+      // second half of the weight fragments
+      __builtin_amdgcn_sched_barrier(0);
+      load_steps(kSteps / 2, kSteps);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < kCPL; ++i) {
     if constexpr (ROT) {
