@@ -203,14 +203,14 @@ hipError_t dispatch_cmax(int cmax, const uint16_t* x, int64_t M, int K, uint8_t*
 }
 
 // Threads per row T (a multiple of 64, at most 256, at most 4 chunks of 32
-// elements per lane).  Small batches need many waves in flight to cover memory
-// latency, large ones are better served by more chunks per lane.  Among the T
-// whose lane slots exceed the row's chunks by at most 25% (fewest slots if
-// none does), take the smallest that gives >= 16 waves per SIMD over the whole
-// batch, or else the largest.  (Measured: 1,502 x 4,096 rotated, 10.4 us with
-// T = 128 against 13.4 us with T = 64; 16,384 x 4,096, 74 us with T = 64
-// against 78 us with T = 128.)  Rows longer than 4 x 256 chunks (K > 32768)
-// use 1024 threads.
+// elements per lane): the largest T whose lane slots exceed the row's chunks by
+// at most 25% (fewest slots if none does) -- fewer chunks per lane means more
+// waves in flight and shorter dependency chains.  (Measured with the current
+// arithmetic: 16,384 x 4,096, 35.5 us with T = 128 against 37.9 us with
+// T = 64; 1,502 x 4,096 rotated, 10.4 us with T = 128 against 13.4 us with
+// T = 64; 12,016 x 17,408 rotated, 197 us with T = 192 (3 chunks) against
+// 354, 300 and 282 us with T = 320, 576 and 1024.)  Rows longer than 4 x 256
+// chunks (K > 32768) use 1024 threads.
 template <bool ROT, bool FP8>
 hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float* s, bool packed,
                          hipStream_t stream) {
@@ -220,7 +220,6 @@ hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float*
     if (cmax > 4) return hipErrorInvalidValue;
     return dispatch_cmax<1024, ROT, FP8>(cmax, x, M, K, q, s, packed, stream);
   }
-  constexpr int64_t kWavesWanted = 16 * 4 * 256;
   int best_t = 0, min_slots_t = 256, min_slots = 1 << 30;
   for (int t = 64; t <= 256; t += 64) {
     const int slots = (nchunks + t - 1) / t * t;
@@ -228,7 +227,6 @@ hipError_t dispatch_rows(const uint16_t* x, int64_t M, int K, uint8_t* q, float*
     if (slots < min_slots) { min_slots = slots; min_slots_t = t; }
     if (4 * slots > 5 * nchunks) continue;                  // more than 25% idle lanes
     best_t = t;
-    if (M * (t / 64) >= kWavesWanted) break;
   }
   if (best_t == 0) best_t = min_slots_t;
   const int cmax = (nchunks + best_t - 1) / best_t;

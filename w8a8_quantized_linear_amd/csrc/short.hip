@@ -321,9 +321,10 @@ hipError_t launch_k(const uint16_t* x, const void* w, bool w_packed, const float
 
 }  // namespace
 
-// One workgroup per CU (~97 KiB of LDS): the single launch pays off while the
-// tiles fit in one round on the 256 CUs (measured: 298 x 1,024 x 1,024 in 13.9 us
-// against 18.3 us for two kernels; 320 tiles of a gate/up shape take 25 us).
+// One workgroup of 4 waves per CU (its registers fill the SIMDs): the single
+// launch pays off while the tiles fit in one round on the 256 CUs, since every
+// tile quantizes its rows again (measured: 298 x 1,024 x 1,024 in 6.8 us per
+// call against 14.1 us for the quantizer and GEMM as two launches).
 bool short_path_fits(int64_t M, int64_t N, int64_t K, Epi epi) {
   if (epi == Epi::kRawI32 || K > kShortMaxK || M > kShortMaxM) return false;
   const int64_t cols = (epi == Epi::kSwiglu) ? kBW / 2 : kBW;
