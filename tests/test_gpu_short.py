@@ -4,7 +4,8 @@ tiles of 32 tokens x 64 weight rows): it must give the same bytes as the two-ker
 quantizer followed by the packed GEMM stage -- for the outputs, the workspace codes
 and the scales, and match the oracle on every element.  Shapes cover ragged M and N,
 the smallest K (one 32-byte step per wave), K with a partial group of 8 chunks, the
-largest K, both weight layouts, rotation on and off, both epilogues."""
+largest K, both weight layouts, rotation on and off, both epilogues, and grids of exactly
+256 tiles."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +34,8 @@ CASES = [
     ("linear", 1, 128, 8, 0, True), ("linear", 31, 384, 72, 128, False), ("linear", 33, 1024, 64, 0, True),
     ("linear", 298, 1024, 1024, 0, True), ("linear", 130, 1024, 200, 128, True), ("linear", 512, 896, 136, 128, False),
     ("gateup", 1, 128, 8, 128, True), ("gateup", 65, 640, 40, 0, True), ("gateup", 300, 1024, 96, 128, False),
+    # exactly 256 tiles, the most the single launch takes (16 x 16 and 8 x 32)
+    ("linear", 512, 1024, 1024, 0, True), ("gateup", 256, 1024, 1024, 128, True),
 ]
 
 
