@@ -206,22 +206,26 @@ def test_pack_weight_layout(lib, rows, K):
         assert not pad.any(), "padding rows must be zero"
 
 
-def _random_shapes(n, seed):
-    """Seeded shapes within the API's rules: M in [1, 700], N a multiple of 8 up to 1,000,
-    K a multiple of 128 up to 1,536; kind and rotation drawn too."""
+def _random_shapes(n, seed, m_range=(1, 701), k_blocks=(1, 13), n_groups=(1, 126)):
+    """Seeded shapes within the API's rules: M in m_range, N a multiple of 8, K a multiple of
+    128 (defaults: M up to 700, N up to 1,000, K up to 1,536 -- mostly short-path sizes);
+    kind, rotation and bias drawn too."""
     rng = np.random.default_rng(seed)
     out = []
     for i in range(n):
         kind = ("linear", "gateup", "fp8")[i % 3]
-        M = int(rng.integers(1, 701))
-        N = int(rng.integers(1, 126)) * 8
-        K = int(rng.integers(1, 13)) * 128
+        M = int(rng.integers(*m_range))
+        N = int(rng.integers(*n_groups)) * 8
+        K = int(rng.integers(*k_blocks)) * 128
         rot = int(rng.integers(0, 2)) * 128
-        out.append(W.custom(kind, M, K, N, rot, bias=bool(rng.integers(0, 2)), seed=100 + i))
+        out.append(W.custom(kind, M, K, N, rot, bias=bool(rng.integers(0, 2)), seed=seed + i))
     return out
 
 
-RANDOM = _random_shapes(9, seed=2026)
+# 48 shapes around the short path's range, 12 with M up to 2,600 (two-kernel path, ragged
+# tiles of every shape)
+RANDOM = (_random_shapes(48, seed=2026) +
+          _random_shapes(12, seed=4052, m_range=(700, 2601), k_blocks=(1, 9), n_groups=(1, 200)))
 
 
 @pytest.mark.parametrize("wl", RANDOM, ids=[w.name for w in RANDOM])
