@@ -70,6 +70,22 @@ SHAPES = [
 ]
 
 
+def _random_shapes(n, seed):
+    """Seeded (M, K, N, rot_in, rot_out, bias) within the entry point's rules: N a multiple
+    of 128 with the output rotation, of 64 without; K a multiple of 128."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        rot_out = int(rng.integers(0, 2)) * 128
+        N = int(rng.integers(1, 13)) * (128 if rot_out else 64)
+        out.append((int(rng.integers(1, 900)), int(rng.integers(1, 7)) * 128, N, int(rng.integers(0, 2)) * 128,
+                    rot_out, bool(rng.integers(0, 2))))
+    return out
+
+
+SHAPES += _random_shapes(8, seed=17)
+
+
 @pytest.mark.parametrize("M,K,N,rot_in,rot_out,has_bias", SHAPES,
                          ids=[f"{m}x{k}x{n}_ri{a}_ro{b}" for m, k, n, a, b, _ in SHAPES])
 def test_stages_against_the_oracle(lib, orc, M, K, N, rot_in, rot_out, has_bias):
