@@ -13,7 +13,10 @@ before the timed region; successive steps rotate through enough copies of them
 (>= 512 MiB in total) that no step finds its operands in the 256 MiB
 last-level cache.
 
-The timed region runs exactly K steps with nothing else enqueued; the same K
+Before timing, W untimed warmup steps run (by default as many as fill about
+0.25 s: the GPU raises its clock over the first tens of milliseconds of
+sustained load, and steps timed inside that ramp run up to 13% slow).  The
+timed region runs exactly K steps with nothing else enqueued; the same K
 steps then run again with HIP events bracketing each kernel on the launch
 stream, which gives the per-kernel average durations (event records idle the
 GPU between kernels, so they stay out of the throughput figure).
@@ -48,13 +51,17 @@ PEAK_FP8_TFLOPS = 5000.0     # dense fp8 MFMA
 PEAK_HBM_GBS = 8000.0        # HBM3E 8 TB/s
 ROTATION_BYTES = 512 << 20
 CALIBRATION_BYTES = 256 << 20   # plain device copy run before the warmup (counter calibration)
+WARMUP_SECONDS = 0.25           # default untimed warmup: the GPU's clock ramps up under load
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warmup steps (default: as many as fill about 0.25 s, at least 40: "
+                         "the GPU raises its clock over the first tens of milliseconds of sustained "
+                         "load, and steps timed before that run up to 13%% slow)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("fused", "unfused", "single", "swiglu-quant", "swiglu-then-quant"),
@@ -323,8 +330,23 @@ def main():
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
-    for i in range(args.warmup):
-        step(i)
+    if args.warmup is not None:
+        warmup = args.warmup
+        for i in range(warmup):
+            step(i)
+    else:
+        # 40 steps, the last 20 timed to estimate a step, then enough more to fill ~0.25 s
+        for i in range(20):
+            step(i)
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        for i in range(20, 40):
+            step(i)
+        torch.cuda.synchronize()
+        per_step = max((time.perf_counter() - t_w) / 20, 1e-6)
+        warmup = 40 + int(WARMUP_SECONDS / per_step)
+        for i in range(40, warmup):
+            step(i)
     torch.cuda.synchronize()
 
     # Timed region: exactly K steps, nothing else enqueued between the kernels.
@@ -364,7 +386,7 @@ def main():
         "unit": "TOPS",
         "n_gpus": 1,
         "steps": args.steps,
-        "warmup": args.warmup,
+        "warmup": warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True,
         "scaling": "weak",
