@@ -32,8 +32,6 @@
 //      thread finishes 8 (SwiGLU: 4) outputs of one row with one store.
 // Every tile quantizes its rows again; this is meant for batches whose whole
 // quantization costs less than a kernel launch.
-#include <type_traits>
-
 #include "epilogue_math.h"
 #include "internal.h"
 #include "quant_math.h"
@@ -146,6 +144,7 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
   const uint16_t* bsrc = bias ? bias : reinterpret_cast<const uint16_t*>(s_ch);
   const uint2 bw0 = *reinterpret_cast<const uint2*>(bsrc + c0);
   const uint2 bw1 = *reinterpret_cast<const uint2*>(bsrc + c1);
+  // (all of the above issued before any row arithmetic)
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- phase 1: quantize rows mb .. mb+31 into LDS --------------------------
