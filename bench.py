@@ -48,6 +48,7 @@ sys.path.insert(0, str(ROOT))
 DEFAULT_WORKLOAD = "rot_1502x4096x4096"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP8_TFLOPS = 5000.0     # dense fp8 MFMA
+PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA (the E4M3FN GEMM runs on it)
 PEAK_HBM_GBS = 8000.0        # HBM3E 8 TB/s
 ROTATION_BYTES = 512 << 20
 CALIBRATION_BYTES = 256 << 20   # plain device copy run before the warmup (counter calibration)
@@ -77,6 +78,10 @@ def parse():
     ap.add_argument("--rot-out", type=int, choices=(0, 128), default=128,
                     help="rotation block of the next linear's input for the swiglu-quant paths "
                          "(the down projection rotates by 128)")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="instead of the workload: the rate the matrix cores sustain with register "
+                         "operands and no memory traffic (int8 32x32x32 and bf16 32x32x16 MFMAs), "
+                         "after a ramp-up launch -- the measured-clock ceiling for the GEMM")
     ap.add_argument("--drift", action="store_true",
                     help="instead of timing: relative L2 drift of every workload's W8A8 output from "
                          "the fp64 unquantized projection, without and with the block rotation")
@@ -190,6 +195,34 @@ def cpu_baseline(wl, inp, unfused=False, rot_out=None):
                       f"{dt:.2f} s wall, {cpu:.1f} s CPU on {threads} threads"}
 
 
+def mfma_peak(torch, lib, blocks=768, launch_s=0.2):
+    """Sustained MFMA rate from the library's register-operand probe: grow the iteration
+    count until a launch takes ~50 ms, run one ~launch_s launch untimed (the clock ramps
+    up under load), then time three and take the median."""
+    import statistics
+    out = {}
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    for kind, ops_each, peak, unit in (("int8", 65536, PEAK_INT8_TOPS, "TOPS"),
+                                       ("bf16", 32768, PEAK_BF16_TFLOPS, "TFLOP/s")):
+        def launch_ms(iters):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            lib.w8a8_mfma_probe(kind, iters, blocks, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+        iters = 256
+        while (ms := launch_ms(iters)) < 50.0:
+            iters *= 4
+        iters = max(1, int(iters * launch_s * 1e3 / ms))
+        launch_ms(iters)                                  # ramp-up, untimed
+        ms = statistics.median(launch_ms(iters) for _ in range(3))
+        rate = blocks * 4 * iters * 4 * ops_each / (ms * 1e-3) / 1e12
+        out[kind] = {"value": rate, "unit": unit, "peak": peak, "frac": rate / peak,
+                     "launch_ms": ms, "iters": iters, "blocks": blocks}
+    return out
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -208,6 +241,9 @@ def main():
     import workloads as W
     import w8a8_quantized_linear_amd as lib
 
+    if args.mfma_peak:
+        print(json.dumps({"mfma_peak": mfma_peak(torch, lib)}))
+        return
     if args.drift:
         import numpy as np
         from w8a8_quantized_linear_amd.drift import drift

@@ -279,6 +279,20 @@ w8a8_status w8a8_gateup_swiglu_quant_packed(const uint16_t* x, const int8_t* w_g
                                             int8_t* q_packed, float* s_tok, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream);
 
+/* ---- measurement aid (not a step of the path; no page describes it) ---------
+ * The rate the matrix cores sustain with operands in registers and no memory
+ * traffic: the ceiling the GEMM's MFMA rate is measured against at the clock
+ * the chip holds under load.  Launches `blocks` workgroups of 4 waves; each
+ * wave runs `iters` rounds of four independent MFMAs -- kind 0: int8
+ * 32x32x32 (65,536 ops each), kind 1: bf16 32x32x16 (32,768 flops each, the
+ * instruction the E4M3FN GEMM runs on) -- alternating between two fixed
+ * operand patterns of the lane index, and stores each lane's accumulator sum
+ * (int32, wrapping) in sink [blocks * 256] (caller-owned, 16-byte aligned).
+ * Ops per launch: blocks * 4 * iters * 4 * (65,536 or 32,768).
+ * 1 <= iters <= 2^40, 1 <= blocks <= 65,536; kind outside {0, 1} is
+ * W8A8_ERR_BAD_ARGUMENT. */
+w8a8_status w8a8_mfma_probe(int kind, int64_t iters, int blocks, int32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

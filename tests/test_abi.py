@@ -55,6 +55,7 @@ def lib():
         "w8a8_gemm_swiglu_blockquant_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, P, P, P]),
         "w8a8_requantize_blocks_packed": (I, [P, P, I64, I64, P, P]),
         "w8a8_gateup_swiglu_quant_packed": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
+        "w8a8_mfma_probe": (I, [I, I64, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -242,3 +243,18 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.w8a8_requantize_blocks_packed(A, A, 4, 256, A, None) == DEVICE
     assert lib.w8a8_gemm_swiglu_blockquant_packed(A, A, A, A, None, 4, 256, 512, 128, A, A, None,
                                                   None) == DEVICE
+
+
+def test_mfma_probe_argument_checks(lib):
+    p = lib.w8a8_mfma_probe
+    assert p(2, 10, 1, A, None) == BADARG          # kind
+    assert p(-1, 10, 1, A, None) == BADARG
+    assert p(0, 0, 1, A, None) == SHAPE            # iters
+    assert p(0, (1 << 40) + 1, 1, A, None) == SHAPE
+    assert p(1, 10, 0, A, None) == SHAPE           # blocks
+    assert p(1, 10, 65537, A, None) == SHAPE
+    assert p(0, 10, 1, None, None) == NULLP
+    assert p(0, 10, 1, A + 4, None) == MISALIGNED
+    import torch
+    if not torch.cuda.is_available():
+        assert p(0, 10, 1, A, None) == DEVICE

@@ -69,6 +69,7 @@ _SIGS = {
     "w8a8_gemm_swiglu_blockquant_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
     "w8a8_requantize_blocks_packed": (_I, [_P, _P, _I64, _I64, _P, _P]),
     "w8a8_gateup_swiglu_quant_packed": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
+    "w8a8_mfma_probe": (_I, [_I, _I64, _I, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -431,3 +432,18 @@ def w8a8_gateup_swiglu_quant_packed(x, w_gateup_packed, N, s_ch, bias=None, rot_
                                                 workspace.numel(), _stream()),
            "w8a8_gateup_swiglu_quant_packed")
     return q, s
+
+
+# ------------------------------------------------------- measurement aid ----
+def w8a8_mfma_probe(kind: str, iters: int, blocks: int = 1024, sink: Optional[torch.Tensor] = None):
+    """MFMA-only rate probe (not a step of the path): kind "int8" (32x32x32) or "bf16"
+    (32x32x16).  Enqueues one launch on the current stream and returns the int32 sink
+    [blocks * 256] (each lane's accumulator sum)."""
+    k = {"int8": 0, "bf16": 1}[kind]
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    _want(sink, torch.int32, "sink", 1)
+    if sink.numel() < blocks * 256:
+        raise ValueError("sink: needs blocks * 256 elements")
+    _check(_lib.w8a8_mfma_probe(k, iters, blocks, _ptr(sink), _stream()), "w8a8_mfma_probe")
+    return sink

@@ -24,7 +24,7 @@ BUILD_DIR = PKG / "_build"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "requant.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "requant.hip", "mfma_probe.hip", "api.cpp"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -363,3 +363,13 @@ w8a8_status w8a8_gateup_swiglu_quant_packed(const uint16_t* x, const int8_t* w_g
 }
 
 }  // extern "C"
+
+w8a8_status w8a8_mfma_probe(int kind, int64_t iters, int blocks, int32_t* sink, hipStream_t stream) {
+  if (kind != 0 && kind != 1) return W8A8_ERR_BAD_ARGUMENT;
+  if (iters < 1 || iters > ((int64_t)1 << 40) || blocks < 1 || blocks > 65536) return W8A8_ERR_BAD_SHAPE;
+  if (!sink) return W8A8_ERR_NULL_POINTER;
+  if (!aligned16(sink)) return W8A8_ERR_MISALIGNED;
+  w8a8_status st;
+  if ((st = check_device()) != W8A8_OK) return st;
+  return launched(w8a8::launch_mfma_probe(kind == 1, iters, blocks, sink, stream));
+}

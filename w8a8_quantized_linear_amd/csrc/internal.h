@@ -68,4 +68,9 @@ hipError_t launch_linear_short(Epi epi, const uint16_t* x, const void* w, bool w
 // Row-major codes [rows, K] -> packed layout (K % 64 == 0; padding rows zero).
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream);
 
+// Measurement aid (not on the path): `blocks` workgroups of 4 waves, each wave
+// `iters` rounds of four independent MFMAs with register operands (int8
+// 32x32x32, or bf16 32x32x16 when bf16); sink [blocks * 256] int32.
+hipError_t launch_mfma_probe(bool bf16, int64_t iters, int blocks, int32_t* sink, hipStream_t stream);
+
 }  // namespace w8a8
