@@ -155,7 +155,7 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> dict:
     f_gemm = sum(fetch[gemm_k]) / len(fetch[gemm_k])
     w_gemm = sum(write[gemm_k]) / len(write[gemm_k])
     rec = {"workload": workload, "sources_digest": kernel_sources_digest(),
-           "gemm_kernel": gemm_k.split("(")[0], "gemm_dispatches": len(fetch[gemm_k]),
+           "gemm_kernel": gemm_k.split(">(")[0].replace("(anonymous namespace)::", "").removeprefix("void ") + ">", "gemm_dispatches": len(fetch[gemm_k]),
            "fetch_kib_per_launch": f_gemm, "write_kib_per_launch": w_gemm,
            "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
            "fetch_factor": f_factor, "write_factor": w_factor,
