@@ -231,3 +231,46 @@ def test_gemm_stages_on_packed_operands(lib, orc, kind, M, N, K):
     ref_fn = {"dequant": orc.gemm_dequant, "swiglu": orc.gemm_swiglu, "fp8": orc.fp8_gemm_dequant}[kind]
     ref = ref_fn(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), W.bits(b))
     compare_bf16(bf16_bits(y), ref, "y")
+
+
+def _pow2(exps) -> torch.Tensor:
+    return torch.tensor([2.0 ** int(e) for e in exps], dtype=torch.float32)
+
+
+@pytest.mark.parametrize("M,N,K,case", [(300, 520, 128, "bias"), (1502, 4096, 128, "packed"),
+                                        (2048, 8192, 128, "subnormal")])
+def test_gemm_dequant_rounding_bit_exact(lib, orc, M, N, K, case):
+    """With power-of-two scales every fp32 step of the dequant epilogue is exact
+    (|acc| < 2^21 at K = 128, so fl32(acc), the scale product and the FMA lose
+    nothing; with the bias, scales >= 1 and integer biases keep the sum below 2^24),
+    so the kernel's bf16 must be the oracle's single rounding of the exact value,
+    bit for bit: round-half-even ties (values with more than 8 significant bits) and,
+    with products of 2^-130 .. 2^-137, bf16 subnormals and underflow to zero.  The
+    shapes run the 128 x 128, 192 x 128 and 256 x 256 tiles."""
+    say(f"gemm_dequant exact rounding M={M} N={N} K={K} {case}")
+    q = W.random_codes((M, K), seed=71 + M)
+    w = W.random_codes((N, K), seed=73 + N)
+    r, c = np.arange(M), np.arange(N)
+    b = None
+    if case == "bias":
+        s_tok, s_ch = _pow2(r % 3), _pow2(c % 2)
+        g = torch.Generator().manual_seed(79)
+        b = torch.randint(-256, 257, (N,), generator=g).to(torch.bfloat16)   # integers, exact in bf16
+    elif case == "packed":
+        s_tok, s_ch = _pow2(r % 3 - 1), _pow2(-(c % 4))
+    else:
+        s_tok, s_ch = _pow2(-62 - r % 4), _pow2(-68 - c % 5)
+    if case == "packed":
+        y = lib.w8a8_gemm_dequant_packed(lib.w8a8_pack_weight(q.cuda()), s_tok.cuda(),
+                                         lib.w8a8_pack_weight(w.cuda()), s_ch.cuda(), K)
+    else:
+        y = lib.w8a8_gemm_dequant(q.cuda(), s_tok.cuda(), w.cuda(), s_ch.cuda(), None if b is None else b.cuda())
+    torch.cuda.synchronize()
+    ref = orc.gemm_dequant(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), None if b is None else W.bits(b))
+    got = bf16_bits(y)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, (f"{bad.size} of {got.size} outputs differ; first at {divmod(int(bad[0]), N)}: "
+                           f"got {got.flat[bad[0]]:#06x}, oracle {ref.flat[bad[0]]:#06x}")
+    if case == "subnormal":   # the case reaches what it is meant to
+        mag = got & 0x7FFF
+        assert ((mag > 0) & (mag < 0x0080)).sum() > 1000 and (mag >= 0x0080).sum() > 1000

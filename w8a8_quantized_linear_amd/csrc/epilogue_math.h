@@ -9,10 +9,15 @@
 
 namespace w8a8 {
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+// Two fp32 values -> two bf16, round to nearest even, low half first.  The
+// kernels run with fp32 denormals preserved and round-to-nearest-even, so the
+// conversion gives the bits of rounding the exact fp32 value for every non-NaN
+// input; gfx950 converts the pair in one instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t bf16x2_rne(float lo, float hi) {
+  const bf16x2_t v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 // Four bf16 values (two 32-bit words) -> fp32.

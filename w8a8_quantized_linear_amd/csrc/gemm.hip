@@ -134,6 +134,16 @@ __device__ __forceinline__ void wait_vmcnt() {
 // registers (the int32 output exists for the exactness tests only).  32x32
 // block layout: lane l holds token column l % 32 and, in registers 4q .. 4q+3,
 // weight rows 8q + 4 * (l / 32) + 0..3 of the block.
+// Workgroup barrier for LDS reuse: this wave's LDS accesses are complete
+// (lgkmcnt(0)) before it arrives, but its global loads and stores may still be
+// in flight (__syncthreads would wait for those too).  The empty asm keeps the
+// compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int TM, int TN, int WTM, int WTN, typename Acc>
 __device__ __forceinline__ void store_tile_i32(const Acc (&acc)[TN][TM], int32_t* __restrict__ out, int64_t M,
                                                int64_t N, int64_t mb, int64_t nb, int wm, int wn, int frag_row,
@@ -175,43 +185,57 @@ __device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], cons
                                                   uint8_t* lds, int tid) {
   constexpr int kStride = 128 * 2 + 16;  // LDS bytes per row of h (padding spreads the banks)
   static_assert(BM * kStride <= LDS_BYTES, "h tile fits the operand ring");
-  __syncthreads();  // every wave is done with the operand ring
+  // scales and bias loaded first, without conditions (as in store_tile_staged)
+  const bool has_bias = bias != nullptr;
+  const uint16_t* bsrc = has_bias ? bias : reinterpret_cast<const uint16_t*>(s_ch);
+  float st[TM];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) st[tm] = s_tok[min<int64_t>(mb + wm * WTM + tm * 32 + frag_row, M - 1)];
+  float4 sg[TN / 2][4], su[TN / 2][4];
+  uint2 bg_raw[TN / 2][4], bu_raw[TN / 2][4];
+#pragma unroll
+  for (int tn = 0; tn < TN / 2; ++tn)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = min<int64_t>(nb + wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half, N - 4);
+      sg[tn][q] = *reinterpret_cast<const float4*>(s_ch + n);
+      su[tn][q] = *reinterpret_cast<const float4*>(s_ch + N + n);
+      bg_raw[tn][q] = *reinterpret_cast<const uint2*>(bsrc + n);
+      bu_raw[tn][q] = *reinterpret_cast<const uint2*>(bsrc + N + n);
+    }
+  lds_barrier();  // every wave is done with the operand ring
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int row_l = wm * WTM + tm * 32 + frag_row;
     const int64_t m = mb + row_l;
     const bool live = m < M;
-    const float st = live ? s_tok[m] : 0.0f;
 #pragma unroll
     for (int tn = 0; tn < TN / 2; ++tn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int col_l = wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half;
         const int64_t n0 = nb + col_l;
-        uint2 hv = make_uint2(0u, 0u);
-        if (live && n0 < N) {
-          const float4 sg = *reinterpret_cast<const float4*>(s_ch + n0);
-          const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n0);
-          float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-          if (bias) {
-            bf16x4(*reinterpret_cast<const uint2*>(bias + n0), bg);
-            bf16x4(*reinterpret_cast<const uint2*>(bias + N + n0), bu);
-          }
-          const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
-          uint16_t o[4];
+        float bg[4], bu[4], y[4];
+        bf16x4(has_bias ? bg_raw[tn][q] : make_uint2(0u, 0u), bg);
+        bf16x4(has_bias ? bu_raw[tn][q] : make_uint2(0u, 0u), bu);
+        const float sgv[4] = {sg[tn][q].x, sg[tn][q].y, sg[tn][q].z, sg[tn][q].w};
+        const float suv[4] = {su[tn][q].x, su[tn][q].y, su[tn][q].z, su[tn][q].w};
 #pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
-            const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
-            o[v] = f32_to_bf16_rne(silu_f32(g) * u);
-          }
-          hv = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
+        for (int v = 0; v < 4; ++v) {
+          const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st[tm] * sgv[v], bg[v]);
+          const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st[tm] * suv[v], bu[v]);
+          y[v] = silu_f32(g) * u;
+        }
+        uint2 hv = make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
+        if (live && n0 < N) {
           if (qo.h) *reinterpret_cast<uint2*>(qo.h + m * N + n0) = hv;
+        } else {
+          hv = make_uint2(0u, 0u);  // columns past N enter the block amax as zeros
         }
         *reinterpret_cast<uint2*>(lds + row_l * kStride + col_l * 2) = hv;
       }
   }
-  __syncthreads();
+  lds_barrier();  // the tile's h is in LDS
 
   const int lane = tid & 63, p = tid & 3;
   const int64_t kblocks = N / 64;
@@ -261,8 +285,8 @@ __device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], cons
 // own LDS region (rows of COLS * 2 bytes, 16-byte chunks XOR-swizzled by row so
 // the 32 rows of a write spread over the banks), then reads it back 16 bytes
 // per lane with consecutive lanes along a row, so each store instruction
-// covers 64 / (COLS / 8) whole row segments.  The caller has made sure that no
-// wave still reads the operand ring (barrier) and passes this wave's region.
+// covers 64 / (COLS / 8) whole row segments.  The region is part of the operand
+// ring: the function waits (barrier) until no wave still reads the ring.
 template <Epi EPI, int TM, int TN, int WTM, int WTN, typename Acc>
 __device__ __forceinline__ void store_tile_staged(const Acc (&acc)[TN][TM], const float* __restrict__ s_tok,
                                                   const float* __restrict__ s_ch,
@@ -274,47 +298,61 @@ __device__ __forceinline__ void store_tile_staged(const Acc (&acc)[TN][TM], cons
   constexpr int ROWB = COLS * 2;                              // bytes per staged row
   constexpr int CPR = ROWB / 16;                              // 16-byte chunks per row
   static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 4, 8 or 16 chunks");
+  constexpr bool kPair = EPI == Epi::kSwiglu;
   const int64_t m0 = mb + (int64_t)wm * WTM, n0w = nb + (int64_t)wn * COLS;
+  // Every scale and bias value the wave needs is loaded first and without
+  // conditions, so that the wave waits for memory once: rows past M read row
+  // M - 1, columns past N the last four (N is a multiple of 8 and a lane's
+  // columns come in fours), and without a bias the loads read s_ch and are
+  // replaced by zeros.  Such values only reach outputs that are never stored.
+  // (Loads under per-element conditions were waited for one at a time: 24
+  // round trips per wave at 192 x 128.)
+  const bool has_bias = bias != nullptr;
+  const uint16_t* bsrc = has_bias ? bias : reinterpret_cast<const uint16_t*>(s_ch);
+  float st[TM];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) st[tm] = s_tok[min<int64_t>(m0 + tm * 32 + frag_row, M - 1)];
+  float4 sg[TNO][4], su[kPair ? TNO : 1][4];
+  uint2 bg_raw[TNO][4], bu_raw[kPair ? TNO : 1][4];
+#pragma unroll
+  for (int tn = 0; tn < TNO; ++tn)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t n = min<int64_t>(n0w + tn * 32 + 8 * q + 4 * frag_half, N - 4);
+      sg[tn][q] = *reinterpret_cast<const float4*>(s_ch + n);
+      bg_raw[tn][q] = *reinterpret_cast<const uint2*>(bsrc + n);
+      if constexpr (kPair) {
+        su[tn][q] = *reinterpret_cast<const float4*>(s_ch + N + n);
+        bu_raw[tn][q] = *reinterpret_cast<const uint2*>(bsrc + N + n);
+      }
+    }
+  lds_barrier();  // every wave is done with the operand ring
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const int row = tm * 32 + frag_row;
-    const int64_t m = m0 + row;
-    const float st = m < M ? s_tok[m] : 0.0f;
 #pragma unroll
     for (int tn = 0; tn < TNO; ++tn)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const int nl = tn * 32 + 8 * q + 4 * frag_half;  // column within the sub-tile
-        const int64_t n = n0w + nl;
-        uint2 hv = make_uint2(0u, 0u);
-        if (m < M && n < N) {
-          uint16_t o[4];
-          if constexpr (EPI == Epi::kDequant) {
-            const float4 sc = *reinterpret_cast<const float4*>(s_ch + n);
-            float bv[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) bf16x4(*reinterpret_cast<const uint2*>(bias + n), bv);
-            const float scv[4] = {sc.x, sc.y, sc.z, sc.w};
+        float bg[4], y[4];
+        bf16x4(has_bias ? bg_raw[tn][q] : make_uint2(0u, 0u), bg);
+        const float sgv[4] = {sg[tn][q].x, sg[tn][q].y, sg[tn][q].z, sg[tn][q].w};
+        if constexpr (!kPair) {
 #pragma unroll
-            for (int v = 0; v < 4; ++v)
-              o[v] = f32_to_bf16_rne(__builtin_fmaf((float)acc[tn][tm][4 * q + v], st * scv[v], bv[v]));
-          } else {  // gate block tn, up block tn + TN/2
-            const float4 sg = *reinterpret_cast<const float4*>(s_ch + n);
-            const float4 su = *reinterpret_cast<const float4*>(s_ch + N + n);
-            float bg[4] = {0.f, 0.f, 0.f, 0.f}, bu[4] = {0.f, 0.f, 0.f, 0.f};
-            if (bias) {
-              bf16x4(*reinterpret_cast<const uint2*>(bias + n), bg);
-              bf16x4(*reinterpret_cast<const uint2*>(bias + N + n), bu);
-            }
-            const float sgv[4] = {sg.x, sg.y, sg.z, sg.w}, suv[4] = {su.x, su.y, su.z, su.w};
+          for (int v = 0; v < 4; ++v) y[v] = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st[tm] * sgv[v], bg[v]);
+        } else {  // gate block tn, up block tn + TN/2
+          float bu[4];
+          bf16x4(has_bias ? bu_raw[tn][q] : make_uint2(0u, 0u), bu);
+          const float suv[4] = {su[tn][q].x, su[tn][q].y, su[tn][q].z, su[tn][q].w};
 #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-              const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
-              const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
-              o[v] = f32_to_bf16_rne(silu_f32(g) * u);
-            }
+          for (int v = 0; v < 4; ++v) {
+            const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st[tm] * sgv[v], bg[v]);
+            const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st[tm] * suv[v], bu[v]);
+            y[v] = silu_f32(g) * u;
           }
-          hv = make_uint2((uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16));
         }
+        const uint2 hv = make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
         const int chunk = nl / 8;  // 16-byte chunk of the row; the lane's 8 bytes are its half frag_half
         *reinterpret_cast<uint2*>(region + row * ROWB + ((chunk ^ (row % CPR)) * 16) + 8 * frag_half) = hv;
       }
@@ -558,7 +596,6 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   } else {
     constexpr int REGION = WTM * (EPI == Epi::kSwiglu ? WTN / 2 : WTN) * 2;
     static_assert(REGION * WGM * WGN <= NST * STAGE, "staged output fits the operand ring");
-    __syncthreads();  // every wave is done with the operand ring
     store_tile_staged<EPI, TM, TN, WTM, WTN>(acc, s_tok, s_ch, bias, static_cast<uint16_t*>(out), M, N, mb, nb,
                                              wm, wn, frag_row, frag_half, lds + wave * REGION, lane);
   }

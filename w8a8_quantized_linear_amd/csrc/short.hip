@@ -279,22 +279,20 @@ linear_short(const uint16_t* __restrict__ x, const uint8_t* __restrict__ w,
   const int32_t sums[8] = {s0[0], s0[1], s0[2], s0[3], s1[0], s1[1], s1[2], s1[3]};
   uint16_t* yrow = y + me * N + n0;
   if constexpr (!SWIGLU) {
-    uint16_t o[8];
+    float o[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) o[e] = f32_to_bf16_rne(__builtin_fmaf((float)sums[e], st * sc[e], bv[e]));
+    for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf((float)sums[e], st * sc[e], bv[e]);
     *reinterpret_cast<u32x4*>(yrow) =
-        u32x4{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16),
-              (uint32_t)o[4] | ((uint32_t)o[5] << 16), (uint32_t)o[6] | ((uint32_t)o[7] << 16)};
+        u32x4{bf16x2_rne(o[0], o[1]), bf16x2_rne(o[2], o[3]), bf16x2_rne(o[4], o[5]), bf16x2_rne(o[6], o[7])};
   } else {
-    uint16_t o[4];
+    float o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const float g = __builtin_fmaf((float)sums[e], st * sc[e], bv[e]);
       const float u = __builtin_fmaf((float)sums[4 + e], st * sc[4 + e], bv[4 + e]);
-      o[e] = f32_to_bf16_rne(silu_f32(g) * u);
+      o[e] = silu_f32(g) * u;
     }
-    *reinterpret_cast<u32x2*>(yrow) =
-        u32x2{(uint32_t)o[0] | ((uint32_t)o[1] << 16), (uint32_t)o[2] | ((uint32_t)o[3] << 16)};
+    *reinterpret_cast<u32x2*>(yrow) = u32x2{bf16x2_rne(o[0], o[1]), bf16x2_rne(o[2], o[3])};
   }
 }
 

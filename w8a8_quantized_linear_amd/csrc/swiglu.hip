@@ -26,7 +26,7 @@ __device__ __forceinline__ uint32_t swiglu_pair(uint32_t gw, uint32_t uw) {
   const float u0 = __uint_as_float(uw << 16), u1 = __uint_as_float(uw & 0xffff0000u);
   const float y0 = silu_f32(g0) * u0;
   const float y1 = silu_f32(g1) * u1;
-  return (uint32_t)f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+  return bf16x2_rne(y0, y1);
 }
 
 __global__ void __launch_bounds__(256)
