@@ -16,10 +16,11 @@ last-level cache.
 Before timing, W untimed warmup steps run (by default as many as fill about
 0.25 s: the GPU raises its clock over the first tens of milliseconds of
 sustained load, and steps timed inside that ramp run up to 13% slow).  The
-timed region runs exactly K steps with nothing else enqueued; the same K
-steps then run again with HIP events bracketing each kernel on the launch
-stream, which gives the per-kernel average durations (event records idle the
-GPU between kernels, so they stay out of the throughput figure).
+timed region runs exactly K steps with nothing else enqueued.  Then each
+library call of the step runs on its own, its K launches back to back between
+two HIP events on the launch stream, which gives the per-kernel average launch
+durations (events between the kernels of a step would idle the GPU for a few
+microseconds each, so they stay out of both measurements).
 
 Other paths (--path): the unfused gate/up chain, the whole-path call as one
 library call, and for gate/up workloads the SwiGLU output quantized for the next
@@ -353,16 +354,10 @@ def main():
             calls[i].append((L.w8a8_quantize_act_packed,
                              (ys[i].data_ptr(), M, n_out, args.rot_out, cs[i].data_ptr(), s2[i].data_ptr(),
                               stream)))
-    n_ev = len(calls[0]) + 1
-
-    def step(i, evs=None):
+    def step(i):
         st = 0
-        for j, (fn, a) in enumerate(calls[i % copies]):
-            if evs is not None:
-                evs[j].record()
+        for fn, a in calls[i % copies]:
             st |= fn(*a)
-        if evs is not None:
-            evs[-1].record()
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
@@ -393,18 +388,28 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    # Per-kernel durations: the same K steps again with HIP events around each
-    # kernel on the launch stream.  (Each event record is a command processor
-    # packet that idles the GPU for a few microseconds between the kernels, so
-    # it is kept out of the throughput measurement above.)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        step(i, evs[i])
-    torch.cuda.synchronize()
+    # Per-kernel durations: each library call of the step on its own, its K
+    # launches of the timed steps (same operand copies, same order) back to back
+    # on the launch stream between two HIP events.  (An event recorded between
+    # the kernels of a step is a command-processor packet that idles the GPU for
+    # a few microseconds, so per-kernel figures get passes of their own.)
+    per_call = []
+    for j in range(len(calls[0])):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        st = 0
+        for i in range(args.steps):
+            fn, a = calls[i % copies][j]
+            st |= fn(*a)
+        e1.record()
+        torch.cuda.synchronize()
+        if st:
+            raise RuntimeError(f"library call failed with status {st}")
+        per_call.append(e0.elapsed_time(e1) / args.steps * 1e-3)
 
     def avg(j):  # s per launch of call j
-        return sum(e[j].elapsed_time(e[j + 1]) for e in evs) / args.steps * 1e-3
+        return per_call[j]
     tq = avg(0)                       # quantizer (or the single whole-path call)
     tg = avg(1) if not single else tq  # GEMM
     ms_per_step = wall / args.steps * 1e3
@@ -450,7 +455,7 @@ def main():
                                      "short batches, else the quantizer and the GEMM")
         out["roofline"]["algorithmic_bytes"] = q_bytes + g_bytes - M * K - 4 * M   # codes not re-read
     if unfused:
-        tsw = sum(e[2].elapsed_time(e[3]) for e in evs) / args.steps * 1e-3
+        tsw = avg(2)
         sw_bytes = 6 * M * n_out                             # read gate + up, write y (bf16)
         out["swiglu"] = {"bound": "hbm", "achieved": sw_bytes / tsw / 1e9, "peak": PEAK_HBM_GBS,
                          "unit": "GB/s", "frac": sw_bytes / tsw / 1e9 / PEAK_HBM_GBS,
