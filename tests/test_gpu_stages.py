@@ -107,6 +107,31 @@ def test_gemm_i32_extremes(lib, orc):
     assert int(acc[0, 0]) == -16129 * K
 
 
+@pytest.mark.parametrize("packed", [False, True])
+def test_gemm_dequant_extremes(lib, orc, packed):
+    """Largest K with extreme codes through the dequant epilogue: |acc| up to 127^2 * 2^17, so
+    fl32(acc) itself rounds; N = 8, the smallest legal width (the epilogue's clamped column
+    loads then stay inside the 8 scales), with a bias."""
+    K, M, N = 131072, 3, 8
+    say(f"gemm_dequant extreme codes K={K} packed={packed}")
+    q = torch.full((M, K), 127, dtype=torch.int8)
+    q[1] = -127
+    q[2, ::2] = -127
+    w = torch.full((N, K), -127, dtype=torch.int8)
+    w[1] = 127
+    w[2, 1::2] = 127
+    w[3] = 0
+    s_tok, s_ch, b = _scales_bias(M, N, 61, bias=True)
+    if packed:
+        y = lib.w8a8_gemm_dequant_packed(lib.w8a8_pack_weight(q.cuda()), s_tok.cuda(), lib.w8a8_pack_weight(w.cuda()),
+                                         s_ch.cuda(), K, bias=b.cuda())
+    else:
+        y = lib.w8a8_gemm_dequant(q.cuda(), s_tok.cuda(), w.cuda(), s_ch.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    ref = orc.gemm_dequant(q.numpy(), s_tok.numpy(), w.numpy(), s_ch.numpy(), W.bits(b))
+    compare_bf16(bf16_bits(y), ref, "y")
+
+
 def _scales_bias(M, Nw, seed, bias=True):
     s_tok = W.random_scales(M, seed=seed)
     s_ch = W.random_scales(Nw, seed=seed + 1, lo=1e-5, hi=1e-3)
