@@ -27,10 +27,10 @@ What each call follows (pages on quantized Clef checkpoints):
 * ``swiglu_bf16`` / ``gateup_unfused`` -- the unfused gate/up path
   ("Loading CLEF INT8", fuse_mlp=False): SwiGLU applied to the separately
   rounded bf16 gate and up projections.
-* ``block_quantize`` / ``requantize_blocks`` / ``gateup_swiglu_quant`` -- the
-  SwiGLU output quantized for the next linear inside the gate/up epilogue, in
-  two steps (128-column blocks on their own scales, then the row scale); the
-  pages do not describe this fusion, the reading is R7 in the C++ header.
+* ``gateup_swiglu_quant`` -- the SwiGLU output handed to the next (down)
+  projection as int8 input: the per-token activation quantizer (INT8 ConvRot
+  card, latency-table notes) applied to the bf16 output of the paired gate/up
+  epilogue, with the next projection's rotation (reading R7 in the C++ header).
 
 No function here carries a "parity unpinned" mark: each is pinned by the
 ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``.
@@ -101,9 +101,6 @@ def _load():
         "orc_fp8_linear": (None, [P, P, P, P, P, I64, I64, I64, I, I]),
         "orc_swiglu_bf16": (None, [P, P, I64, P, I64, I64, I]),
         "orc_gateup_unfused": (None, [P, P, P, P, P, I64, I64, I64, I, I]),
-        "orc_col_blocks": (I64, [I64]),
-        "orc_block_quantize": (None, [P, I64, I64, I, P, P, I]),
-        "orc_requantize_blocks": (None, [P, P, I64, I64, P, P, I]),
         "orc_gateup_swiglu_quant": (None, [P, P, P, P, P, P, I64, I64, I64, I, I, I]),
     }
     for name, (res, args) in sigs.items():
@@ -319,39 +316,9 @@ def gateup_unfused(x, w_gateup, s_ch, bias=None, rot_block=0, threads=None):
 
 
 # ------------------------------------ SwiGLU output quantized for the next linear --
-def col_blocks(N: int) -> int:
-    """Number of 128-column blocks of an N-column row (the last may be shorter)."""
-    return int(_load().orc_col_blocks(N))
-
-
-def block_quantize(h, rot_block=0, threads=None):
-    """Step 1: each 128-column block of each row of h (bf16 bits [M, N]) rotated
-    (or not) and quantized on its own: returns (qb int8 [M, N], amax fp32 [M, nblk])."""
-    lib = _load()
-    h = np.ascontiguousarray(h, dtype=np.uint16)
-    M, N = h.shape
-    qb = np.empty((M, N), dtype=np.int8)
-    amax = np.empty((M, col_blocks(N)), dtype=np.float32)
-    lib.orc_block_quantize(_ptr(h), M, N, rot_block, _ptr(qb), _ptr(amax), threads or default_threads())
-    return qb, amax
-
-
-def requantize_blocks(qb, amax, threads=None):
-    """Step 2: block codes rescaled to the row scale: returns (q int8 [M, N], s fp32 [M])."""
-    lib = _load()
-    qb = np.ascontiguousarray(qb)
-    M, N = qb.shape
-    qb = _check(qb, np.int8, (M, N), "qb")
-    amax = _check(amax, np.float32, (M, col_blocks(N)), "amax")
-    q = np.empty((M, N), dtype=np.int8)
-    s = np.empty((M,), dtype=np.float32)
-    lib.orc_requantize_blocks(_ptr(qb), _ptr(amax), M, N, _ptr(q), _ptr(s), threads or default_threads())
-    return q, s
-
-
 def gateup_swiglu_quant(x, w_gateup, s_ch, bias=None, rot_in=0, rot_out=0, threads=None):
-    """Gate/up SwiGLU whose output is quantized for the next linear (two steps,
-    block then row scale): returns (q int8 [M, N], s fp32 [M])."""
+    """Gate/up SwiGLU whose bf16 output goes through the per-token int8 quantizer of
+    the next linear (rotation rot_out): returns (q int8 [M, N], s fp32 [M])."""
     lib = _load()
     M, K = x.shape
     Nw = w_gateup.shape[0]

@@ -35,18 +35,13 @@
 //       to bf16 (round half to even).
 //   R6  SwiGLU: g, u = the unrounded epilogue values of packed rows n and
 //       N + n; output bf16(g * sigmoid(g) * u) evaluated in fp64.
-//   R7  quantizing the SwiGLU output for the next linear inside the gate/up
-//       epilogue (no page describes it; it is the fused form of running the
-//       per-token quantizer on the SwiGLU output): a row's codes need its
-//       amax over all columns, which one output tile does not see.  So each
-//       block of 128 columns (the rotation block; the last one may be
-//       shorter without rotation) is first quantized on its own scale
-//       s_b = fl32(amax_b / 127) as in R1, R3, R4; then the row scale is
-//       s = fl32(max_b amax_b / 127) -- the per-token scale of the whole row
-//       exactly -- and each block's codes are rescaled:
-//       rho_b = fl32(s_b / s) (0 when s = 0), q = round-half-even(fl32(q_b * rho_b)).
-//       The block holding the row's amax keeps its codes (rho = 1); the
-//       others differ from single rounding by at most one step.
+//   R7  the SwiGLU output handed to the next (down) projection as int8 input:
+//       that projection's activations go through the same per-token activation
+//       quantizer as every INT8 projection ("CLEF Calibrated INT8 ConvRot"
+//       card, notes under the latency table), applied to the bf16 output of
+//       the paired gate/up epilogue ("Loading CLEF INT8", fuse_mlp): q, s =
+//       the R1/R3/R4 quantizer of bf16(silu(g) * u), with the next
+//       projection's rotation.  One rounding per code, as for any activation.
 //
 // Every function is plain loops.  Threads split independent rows/elements
 // only; no arithmetic is blocked, fused or reordered.
@@ -472,68 +467,16 @@ void orc_gateup_unfused(const uint16_t* x, const int8_t* w, const float* s_ch, c
   orc_swiglu_bf16(h.data(), h.data() + N, 2 * N, y, M, N, nthreads);
 }
 
-// ---- quantizing the SwiGLU output for the next linear (R7) ----
-// Blocks of 128 columns: block b covers [128 b, min(128 b + 128, N)); with
-// rotation every block is whole (N % 128 == 0).
-int64_t orc_col_blocks(int64_t N) { return (N + 127) / 128; }
-
-// Step 1: h bf16 [M, N] -> block codes qb int8 [M, N] and block amax [M, nblk].
-void orc_block_quantize(const uint16_t* h, int64_t M, int64_t N, int rot_block, int8_t* qb,
-                        float* amax, int nthreads) {
-  check_rounding_mode();
-  require(rot_block == 0 || N % 128 == 0, "rotation blocks of 128 dividing N");
-  const int64_t nblk = orc_col_blocks(N);
-  parallel_for(M, nthreads, [&](int64_t lo, int64_t hi) {
-    float y[128];
-    for (int64_t m = lo; m < hi; ++m) {
-      for (int64_t b = 0; b < nblk; ++b) {
-        const int64_t c0 = 128 * b, len = std::min<int64_t>(128, N - c0);
-        rotate_row(h + m * N + c0, len, rot_block, y);
-        float a = 0.0f;
-        for (int64_t k = 0; k < len; ++k) a = std::max(a, std::fabs(y[k]));
-        amax[m * nblk + b] = a;
-        float s_b;
-        quantize_row_i8(y, len, qb + m * N + c0, &s_b);  // codes at s_b = fl32(a / 127)
-      }
-    }
-  });
-}
-
-// Step 2: block codes + block amax -> codes q int8 [M, N] on the row scale s [M].
-void orc_requantize_blocks(const int8_t* qb, const float* amax, int64_t M, int64_t N, int8_t* q,
-                           float* s, int nthreads) {
-  check_rounding_mode();
-  const int64_t nblk = orc_col_blocks(N);
-  parallel_for(M, nthreads, [&](int64_t lo, int64_t hi) {
-    for (int64_t m = lo; m < hi; ++m) {
-      float a = 0.0f;
-      for (int64_t b = 0; b < nblk; ++b) a = std::max(a, amax[m * nblk + b]);
-      const float s_row = a / 127.0f;
-      s[m] = s_row;
-      for (int64_t b = 0; b < nblk; ++b) {
-        const float s_b = amax[m * nblk + b] / 127.0f;
-        const float rho = s_row > 0.0f ? s_b / s_row : 0.0f;
-        const int64_t c0 = 128 * b, c1 = std::min<int64_t>(c0 + 128, N);
-        for (int64_t c = c0; c < c1; ++c) {
-          const float t = (float)qb[m * N + c] * rho;
-          q[m * N + c] = (int8_t)std::nearbyint(t);  // |t| <= 127: no clamp needed
-        }
-      }
-    }
-  });
-}
-
-// Whole: x -> gate/up SwiGLU (rotation rot_in on x) -> codes and scales of the
-// SwiGLU output for a next linear that rotates its input by rot_out.
+// ---- the SwiGLU output quantized for the next linear (R7) ----
+// Whole: x -> gate/up SwiGLU (rotation rot_in on x) -> the per-token quantizer of
+// the bf16 SwiGLU output, with the next linear's rotation rot_out: codes q [M, N]
+// and scales s [M].
 void orc_gateup_swiglu_quant(const uint16_t* x, const int8_t* w, const float* s_ch,
                              const uint16_t* bias, int8_t* q, float* s, int64_t M, int64_t N,
                              int64_t K, int rot_in, int rot_out, int nthreads) {
   std::vector<uint16_t> h((size_t)(M * N));
   orc_gateup_swiglu(x, w, s_ch, bias, h.data(), M, N, K, rot_in, nthreads);
-  std::vector<int8_t> qb((size_t)(M * N));
-  std::vector<float> amax((size_t)(M * orc_col_blocks(N)));
-  orc_block_quantize(h.data(), M, N, rot_out, qb.data(), amax.data(), nthreads);
-  orc_requantize_blocks(qb.data(), amax.data(), M, N, q, s, nthreads);
+  orc_quantize_i8(h.data(), M, N, rot_out, q, s, nthreads);
 }
 
 void orc_fp8_linear(const uint16_t* x, const uint8_t* w, const float* s_ch, const uint16_t* bias,

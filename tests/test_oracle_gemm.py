@@ -108,6 +108,56 @@ def test_dequant_exact_rational(orc):
     assert not np.array_equal(y0, y)
 
 
+def _e4m3_values(codes):
+    return torch.from_numpy(np.ascontiguousarray(codes)).view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_fp8_dequant_exact_rational(orc):
+    """E4M3FN epilogue ("clef-flash-FP8" card, Quantization table: FP8 W8A8 with
+    per-token and per-channel scales): y = bf16(sum_k dec(q) dec(w) * s_tok * s_ch + b)
+    with one rounding, codes decoded by torch's float8_e4m3fn and the sum, products
+    and bias taken as exact rationals."""
+    M, N, K = 5, 24, 256
+    g = np.random.default_rng(73)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    q = g.choice(codes, (M, K)).astype(np.uint8)
+    w = g.choice(codes, (N, K)).astype(np.uint8)
+    q[1, :] = 0x38                                   # a row of 1.0: the sum is that of w's row
+    s_tok = W.random_scales(M, seed=74, lo=1e-3, hi=1.0).numpy()
+    s_ch = W.random_scales(N, seed=75, lo=1e-4, hi=1e-2).numpy()
+    bias = W.bits((torch.randn(N, generator=torch.Generator().manual_seed(76)) * 0.05).to(torch.bfloat16))
+    y = orc.fp8_gemm_dequant(q, s_tok, w, s_ch, bias)
+    dq, dw = _e4m3_values(q), _e4m3_values(w)
+    b = _bf16_to_f64(bias)
+    for m in range(M):
+        for n in range(N):
+            dot = sum((Fraction(float(a)) * Fraction(float(c)) for a, c in zip(dq[m], dw[n])), Fraction(0))
+            v = dot * Fraction(float(s_tok[m])) * Fraction(float(s_ch[n])) + Fraction(float(b[n]))
+            assert int(y[m, n]) == _nearest_bf16_fraction(v), (m, n)
+    # and without a bias the same rational minus b
+    y0 = orc.fp8_gemm_dequant(q, s_tok, w, s_ch, None)
+    dot = sum((Fraction(float(a)) * Fraction(float(c)) for a, c in zip(dq[2], dw[3])), Fraction(0))
+    assert int(y0[2, 3]) == _nearest_bf16_fraction(dot * Fraction(float(s_tok[2])) * Fraction(float(s_ch[3])))
+
+
+def test_fp8_linear_through_the_exact_epilogue(orc):
+    """The whole fp8 path = the (pinned) E4M3FN quantizer's codes and scales through
+    the exact-rational epilogue above, on a small rotated workload."""
+    wl = W.custom("fp8", 4, 256, 16, 128, bias=True, seed=77)
+    inp = W.make_inputs(wl)
+    x, w, bias = W.bits(inp.x), W.bits(inp.w), W.bits(inp.bias)
+    wq, s_ch = orc.quantize_fp8(w, 128)
+    qx, s_tok = orc.quantize_fp8(x, 128)
+    y = orc.fp8_linear(x, wq, s_ch, bias, 128)
+    dq, dw = _e4m3_values(qx), _e4m3_values(wq)
+    b = _bf16_to_f64(bias)
+    for m in range(4):
+        for n in range(16):
+            dot = sum((Fraction(float(a)) * Fraction(float(c)) for a, c in zip(dq[m], dw[n])), Fraction(0))
+            v = dot * Fraction(float(s_tok[m])) * Fraction(float(s_ch[n])) + Fraction(float(b[n]))
+            assert int(y[m, n]) == _nearest_bf16_fraction(v), (m, n)
+
+
 def test_swiglu_packing_and_values(orc):
     M, N, K = 5, 24, 256
     q = W.random_codes((M, K), seed=51).numpy()
