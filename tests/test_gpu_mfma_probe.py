@@ -1,8 +1,9 @@
-"""The MFMA rate probe (a measurement aid, not a step of the path) computes what it
-claims: every wave's accumulator total equals the closed form iters * sum over chains c,
-lane halves h and positions t of (sum of operand A over the half's 32 lanes) times (sum of
-operand B over them) -- exact, for int8 (32x32x32) and bf16 (32x32x16) with small
-integer operands.  The operand formulas are the kernel's."""
+"""The MFMA rate probe (a measurement aid in the bench-only probe library, not a step
+of the path) computes what it claims: every wave's accumulator total equals the
+closed form iters * sum over chains c, lane halves h and positions t of (sum of
+operand A over the half's 32 lanes) times (sum of operand B over them) -- exact, for
+int8 (32x32x32) and bf16 (32x32x16) with small integer operands.  The operand
+formulas are the kernel's."""
 import numpy as np
 import pytest
 import torch
@@ -11,11 +12,11 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(scope="module")
-def lib():
+def probe():
     if not torch.cuda.is_available():
         pytest.fail("GPU tests need a HIP device")
-    import w8a8_quantized_linear_amd as lib
-    return lib
+    import w8a8_quantized_linear_amd.probe as probe
+    return probe
 
 
 def _i8(lane, s, t, which):
@@ -40,9 +41,9 @@ def _wave_total(kind, iters):
 
 
 @pytest.mark.parametrize("kind", ["int8", "bf16"])
-def test_probe_accumulates_the_closed_form(lib, kind):
+def test_probe_accumulates_the_closed_form(probe, kind):
     iters, blocks = 5, 3
-    sink = lib.w8a8_mfma_probe(kind, iters, blocks)
+    sink = probe.mfma_rate(kind, iters, blocks)
     torch.cuda.synchronize()
     per_lane = sink.cpu().numpy().astype(np.int64).reshape(blocks * 4, 64)
     want = _wave_total(kind, iters)

@@ -24,7 +24,11 @@ BUILD_DIR = PKG / "_build"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "requant.hip", "mfma_probe.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "api.cpp"]
+# measurement aids for the benchmark and the design tests (not the library's C ABI)
+PROBE_DIR = PKG / "probe"
+PROBE_SOURCES = ["mfma_probe.hip", "fp8_contraction.hip"]
+PROBE_LIB = PROBE_DIR / "libw8a8_probe.so"
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -35,11 +39,11 @@ COMMON = [
 ]
 
 
-def _compile(src: str) -> Path:
-    obj = BUILD_DIR / (src.rsplit(".", 1)[0] + ".o")
+def _compile(src: str, folder: Path = CSRC, tag: str = "") -> Path:
+    obj = BUILD_DIR / (tag + src.rsplit(".", 1)[0] + ".o")
     obj.unlink(missing_ok=True)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", str(CSRC / src), "-o", str(obj)]
+    cmd = [HIPCC, *COMMON, *lang, "-c", str(folder / src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
@@ -50,11 +54,8 @@ def _compile(src: str) -> Path:
     return obj
 
 
-def build() -> Path:
-    BUILD_DIR.mkdir(exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB.with_suffix(".so.tmp")
+def _link(objs, out: Path) -> Path:
+    tmp = out.with_suffix(".so.tmp")
     cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *map(str, objs), "-o", str(tmp)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -64,7 +65,18 @@ def build() -> Path:
     missing = [l for l in nm.stdout.splitlines() if "__device_stub__" in l]
     if nm.returncode != 0 or missing:
         raise RuntimeError("link produced a library with undefined kernel stubs:\n" + "\n".join(missing))
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+    return out
+
+
+def build() -> Path:
+    """Build libw8a8.so (the library) and probe/libw8a8_probe.so (measurement aids)."""
+    BUILD_DIR.mkdir(exist_ok=True)
+    jobs = [(src, CSRC, "") for src in SOURCES] + [(src, PROBE_DIR, "probe_") for src in PROBE_SOURCES]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(*j), jobs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

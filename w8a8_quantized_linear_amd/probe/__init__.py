@@ -1,0 +1,67 @@
+"""Measurement aids for the benchmark and the design tests -- not part of the
+W8A8 path and not part of the library's C ABI (``include/w8a8.h``).
+
+``libw8a8_probe.so`` (built next to this file by ``w8a8_quantized_linear_amd/build.py``)
+holds two kernels:
+
+* ``mfma_rate`` -- the rate the matrix cores sustain with register operands and no
+  memory traffic (int8 32x32x32 or bf16 32x32x16 MFMAs): the measured-clock
+  ceiling the GEMM is set against (``bench.py --mfma-peak``);
+* ``fp8_contraction`` -- an E4M3FN x E4M3FN contraction through the fp8 matrix
+  instructions, or through exact widening to bf16, for measuring how accurately
+  each sums its products.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+LIB_PATH = Path(__file__).resolve().parent / "libw8a8_probe.so"
+if not LIB_PATH.exists():
+    raise ImportError(f"{LIB_PATH} is not built; run `python w8a8_quantized_linear_amd/build.py`")
+_lib = ctypes.CDLL(str(LIB_PATH))
+_lib.w8a8_probe_mfma_rate.restype = ctypes.c_int
+_lib.w8a8_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+_lib.w8a8_probe_fp8_contraction.restype = ctypes.c_int
+_lib.w8a8_probe_fp8_contraction.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                            ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+
+FP8_KINDS = {"fp8_32x32x16": 0, "f8f6f4_32x32x64": 1, "fp8_32x32x16_fp32_adds": 2, "bf16_widened": 3}
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def mfma_rate(kind: str, iters: int, blocks: int = 1024, sink: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One launch of the rate probe on the current stream: kind "int8" or "bf16".
+    Returns the int32 sink [blocks * 256] (each lane's accumulator sum)."""
+    k = {"int8": 0, "bf16": 1}[kind]
+    if sink is None:
+        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    if sink.dtype != torch.int32 or not sink.is_cuda or not sink.is_contiguous() or sink.numel() < blocks * 256:
+        raise ValueError("sink: a contiguous int32 device tensor of blocks * 256 elements")
+    if _lib.w8a8_probe_mfma_rate(k, iters, blocks, sink.data_ptr(), _stream()) != 0:
+        raise RuntimeError("w8a8_probe_mfma_rate: bad argument or launch failure")
+    return sink
+
+
+def fp8_contraction(kind: str, a: torch.Tensor, b: torch.Tensor) -> torch.Tensor:
+    """C fp32 [M, N] = dec(a) . dec(b)^T for E4M3FN codes a [M, K], b [N, K] (uint8,
+    contiguous, on the device; M, N multiples of 32, K of 64) through the route
+    ``kind`` (a key of FP8_KINDS)."""
+    for t, name in ((a, "a"), (b, "b")):
+        if t.dtype != torch.uint8 or t.dim() != 2 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name}: a contiguous 2-D uint8 device tensor")
+    M, K = a.shape
+    N = b.shape[0]
+    if b.shape[1] != K:
+        raise ValueError("a and b disagree on K")
+    c = torch.empty((M, N), dtype=torch.float32, device=a.device)
+    if _lib.w8a8_probe_fp8_contraction(FP8_KINDS[kind], a.data_ptr(), b.data_ptr(), c.data_ptr(), M, N, K,
+                                       _stream()) != 0:
+        raise RuntimeError("w8a8_probe_fp8_contraction: unsupported shape or launch failure")
+    return c

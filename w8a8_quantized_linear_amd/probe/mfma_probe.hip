@@ -12,9 +12,9 @@
 // (sum_l b_{c/2}(l, t)) with l over the 32 lanes of half h -- whatever the
 // hardware's row, column and k order, as long as A and B pair k by lane half and
 // position, which the GEMM relies on too.
-#include "internal.h"
+#include <hip/hip_runtime.h>
+#include <cstdint>
 
-namespace w8a8 {
 namespace {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -87,12 +87,17 @@ __global__ void __launch_bounds__(256) mfma_probe_kernel(int64_t iters, int32_t*
 
 }  // namespace
 
-hipError_t launch_mfma_probe(bool bf16, int64_t iters, int blocks, int32_t* sink, hipStream_t stream) {
-  if (bf16)
+// Launches `blocks` workgroups of 4 waves; each wave runs `iters` rounds of four
+// independent MFMAs (kind 0: int8 32x32x32, 65,536 ops each; kind 1: bf16
+// 32x32x16, 32,768 flops each) and stores each lane's accumulator sum in sink
+// [blocks * 256] (int32).  Ops per launch: blocks * 4 * iters * 4 * ops each.
+// Returns 0, or -1 for a bad argument (1 <= iters <= 2^40, 1 <= blocks <= 65536).
+extern "C" int w8a8_probe_mfma_rate(int kind, int64_t iters, int blocks, int32_t* sink, hipStream_t stream) {
+  if ((kind != 0 && kind != 1) || iters < 1 || iters > ((int64_t)1 << 40) || blocks < 1 || blocks > 65536 || !sink)
+    return -1;
+  if (kind == 1)
     hipLaunchKernelGGL(mfma_probe_kernel<true>, dim3(blocks), dim3(256), 0, stream, iters, sink);
   else
     hipLaunchKernelGGL(mfma_probe_kernel<false>, dim3(blocks), dim3(256), 0, stream, iters, sink);
-  return hipGetLastError();
+  return hipGetLastError() == hipSuccess ? 0 : -2;
 }
-
-}  // namespace w8a8
