@@ -22,11 +22,14 @@ two HIP events on the launch stream, which gives the per-kernel average launch
 durations (events between the kernels of a step would idle the GPU for a few
 microseconds each, so they stay out of both measurements).
 
+Before the warmup steps, steps run untimed for about 0.3 s whatever W is (the
+clock ramp; reported as ``clock_ramp_steps``), so that an explicit small W does
+not put the timed steps inside the ramp.
+
 Other paths (--path): the unfused gate/up chain, the whole-path call as one
 library call, and for gate/up workloads the SwiGLU output quantized for the next
-linear either inside the GEMM epilogue (swiglu-quant: block codes, then the
-rescaling pass) or by the per-token quantizer after the bf16 output
-(swiglu-then-quant); the ops counted stay those of the GEMM.
+linear (swiglu-quant: the three kernels of ``w8a8_gateup_swiglu_quant_packed``);
+the ops counted stay those of the GEMM.
 
 Prints one JSON line: metric = TOPS of the whole path (2*M*N_w*K ops per step
 over the step time), the roofline of the dominant kernel (the GEMM) with its
@@ -46,7 +49,7 @@ from pathlib import Path
 ROOT = Path(__file__).resolve().parent
 sys.path.insert(0, str(ROOT))
 
-DEFAULT_WORKLOAD = "rot_1502x4096x4096"
+DEFAULT_WORKLOAD = "down_12016x17408x5120"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_FP8_TFLOPS = 5000.0     # dense fp8 MFMA
 PEAK_BF16_TFLOPS = 2500.0    # dense bf16 MFMA (the E4M3FN GEMM runs on it)
@@ -54,6 +57,13 @@ PEAK_HBM_GBS = 8000.0        # HBM3E 8 TB/s
 ROTATION_BYTES = 512 << 20
 CALIBRATION_BYTES = 256 << 20   # plain device copy run before the warmup (counter calibration)
 WARMUP_SECONDS = 0.25           # default untimed warmup: the GPU's clock ramps up under load
+RAMP_SECONDS = 0.3              # untimed steps before the warmup steps (clock ramp), always run
+# Context only (not this metric): the INT8 card's whole-model batch-1 forward on an H100
+# 80 GB at 2,270 tokens ("CLEF Calibrated INT8 ConvRot" card, latency table).
+H100_CONTEXT = {"hardware": "H100 80 GB", "workload": "whole model, batch 1, 2,270 input tokens",
+                "int8_cute_ms": 170.62, "bf16_ms": 241.09,
+                "source": "CLEF Calibrated INT8 ConvRot card, latency table",
+                "note": "context only: a whole-model latency, not a measurement of this kernel path"}
 
 
 def parse():
@@ -66,18 +76,17 @@ def parse():
                          "load, and steps timed before that run up to 13%% slow)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--path", choices=("fused", "unfused", "single", "swiglu-quant", "swiglu-then-quant"),
+    ap.add_argument("--path", choices=("fused", "unfused", "single", "swiglu-quant"),
                     default="fused",
                     help="fused: quantizer and GEMM with its fused epilogue, timed per kernel; "
                          "unfused (gate/up workloads): the fuse_mlp=False chain -- GEMM onto the 2N "
                          "packed rows with the dequant epilogue, then w8a8_swiglu; single (int8): "
                          "the whole-path entry point as one call (one kernel for short batches); "
                          "swiglu-quant (gate/up): the SwiGLU output quantized for the next linear "
-                         "inside the GEMM epilogue (block codes), then the rescaling pass; "
-                         "swiglu-then-quant (gate/up): the same codes' reference route -- fused "
-                         "SwiGLU GEMM writing bf16, then the per-token quantizer on it")
+                         "(w8a8_gateup_swiglu_quant_packed: the fused SwiGLU GEMM writing bf16 h, then "
+                         "the per-token quantizer on h)")
     ap.add_argument("--rot-out", type=int, choices=(0, 128), default=128,
-                    help="rotation block of the next linear's input for the swiglu-quant paths "
+                    help="rotation block of the next linear's input for the swiglu-quant path "
                          "(the down projection rotates by 128)")
     ap.add_argument("--mfma-peak", action="store_true",
                     help="instead of the workload: the rate the matrix cores sustain with register "
@@ -191,16 +200,20 @@ def cpu_baseline(wl, inp, unfused=False, rot_out=None):
             break
     dt, cpu = time.perf_counter() - t0, time.process_time() - c0
     ops = 2 * rows * wl.n_w * wl.K * passes
-    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+    host_cores = os.cpu_count() or 1
+    return {"value": ops / dt / 1e12, "unit": "TOPS", "cores": threads, "host_cores": host_cores,
+            "threads": threads, "kind": "oracle",
             "sample": f"{rows} of {wl.M} token rows, {passes} pass(es) (quantize + GEMM + epilogue), "
-                      f"{dt:.2f} s wall, {cpu:.1f} s CPU on {threads} threads"}
+                      f"{dt:.2f} s wall, {cpu:.1f} s CPU on {threads} threads of a {host_cores}-core host "
+                      "(the threads are the process's CPU share)"}
 
 
-def mfma_peak(torch, lib, blocks=768, launch_s=0.2):
-    """Sustained MFMA rate from the library's register-operand probe: grow the iteration
+def mfma_peak(torch, blocks=768, launch_s=0.2):
+    """Sustained MFMA rate from the register-operand probe (bench-only probe library): grow the iteration
     count until a launch takes ~50 ms, run one ~launch_s launch untimed (the clock ramps
     up under load), then time three and take the median."""
     import statistics
+    import w8a8_quantized_linear_amd.probe as probe
     out = {}
     sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
     for kind, ops_each, peak, unit in (("int8", 65536, PEAK_INT8_TOPS, "TOPS"),
@@ -208,7 +221,7 @@ def mfma_peak(torch, lib, blocks=768, launch_s=0.2):
         def launch_ms(iters):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
-            lib.w8a8_mfma_probe(kind, iters, blocks, sink)
+            probe.mfma_rate(kind, iters, blocks, sink)
             e1.record()
             torch.cuda.synchronize()
             return e0.elapsed_time(e1)
@@ -243,7 +256,7 @@ def main():
     import w8a8_quantized_linear_amd as lib
 
     if args.mfma_peak:
-        print(json.dumps({"mfma_peak": mfma_peak(torch, lib)}))
+        print(json.dumps({"mfma_peak": mfma_peak(torch)}))
         return
     if args.drift:
         import numpy as np
@@ -275,8 +288,7 @@ def main():
     unfused = args.path == "unfused"
     single = args.path == "single"
     quantout = args.path == "swiglu-quant"
-    then_quant = args.path == "swiglu-then-quant"
-    if (unfused or quantout or then_quant) and wl.kind != "gateup":
+    if (unfused or quantout) and wl.kind != "gateup":
         print(f"bench.py: --path {args.path} applies to gate/up workloads only", file=sys.stderr)
         sys.exit(2)
     if single and wl.kind == "fp8":
@@ -304,12 +316,10 @@ def main():
     ys = [torch.empty((M, n_out), dtype=torch.bfloat16, device=dev) for _ in range(copies)]
     # unfused: the bf16 gate/up projection [M, 2N] between the GEMM and the SwiGLU pass
     hs = [torch.empty((M, Nw), dtype=torch.bfloat16, device=dev) for _ in range(copies)] if unfused else []
-    # swiglu-quant paths: the next linear's input codes (packed) + scales, and the block amax
-    nblk = (n_out + 127) // 128
-    if quantout or then_quant:
+    # swiglu-quant: the next linear's input codes (packed) + scales
+    if quantout:
         cs = [torch.empty((lib.packed_bytes(M, n_out),), dtype=torch.int8, device=dev) for _ in range(copies)]
         s2 = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(copies)]
-        am = [torch.empty((M, nblk), dtype=torch.float32, device=dev) for _ in range(copies)] if quantout else []
     torch.cuda.synchronize()
 
     L = lib._lib
@@ -341,15 +351,7 @@ def main():
         pfn = L.w8a8_linear_packed if wl.kind == "linear" else L.w8a8_gateup_swiglu_packed
         calls = [[(pfn, (xs[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, ys[i].data_ptr(), M, n_out, K,
                          wl.rot_block, wss[i].data_ptr(), wsz, stream))] for i in range(copies)]
-    if quantout:
-        calls = [[(qfn, qargs[i]),
-                  (L.w8a8_gemm_swiglu_blockquant_packed,
-                   (qs[i].data_ptr(), ss[i].data_ptr(), wqs[i].data_ptr(), sch, bptr, M, n_out, K,
-                    args.rot_out, cs[i].data_ptr(), am[i].data_ptr(), None, stream)),
-                  (L.w8a8_requantize_blocks_packed,
-                   (cs[i].data_ptr(), am[i].data_ptr(), M, n_out, s2[i].data_ptr(), stream))]
-                 for i in range(copies)]
-    if then_quant:
+    if quantout:   # the kernels w8a8_gateup_swiglu_quant_packed enqueues, h in ys
         for i in range(copies):
             calls[i].append((L.w8a8_quantize_act_packed,
                              (ys[i].data_ptr(), M, n_out, args.rot_out, cs[i].data_ptr(), s2[i].data_ptr(),
@@ -361,6 +363,13 @@ def main():
         if st:
             raise RuntimeError(f"library call failed with status {st}")
 
+    # clock ramp: untimed steps for about RAMP_SECONDS, whatever the warmup count
+    t_r, ramp = time.perf_counter(), 0
+    while time.perf_counter() - t_r < RAMP_SECONDS:
+        for _ in range(8):
+            step(ramp)
+            ramp += 1
+        torch.cuda.synchronize()
     if args.warmup is not None:
         warmup = args.warmup
         for i in range(warmup):
@@ -416,7 +425,7 @@ def main():
     ops = 2 * M * Nw * K
     q_bytes = 2 * M * K + M * K + 4 * M                      # read bf16 x, write codes + scales
     out_cols = Nw if unfused else n_out                      # the unfused GEMM writes [M, 2N]
-    out_bytes = M * n_out + 4 * M * nblk if quantout else M * out_cols * 2   # block codes + amax, or bf16
+    out_bytes = M * out_cols * 2                             # bf16 output
     g_bytes = M * K + Nw * K + 4 * (M + Nw) + out_bytes + (0 if bias0 is None else 2 * Nw)
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
     traffic = stored_traffic(wl.name + ("-unfused" if unfused else "") + ("-swiglu-quant" if quantout else ""))
@@ -437,9 +446,9 @@ def main():
         "config": {"workload": wl.name, "M": M, "K": K, "N": n_out, "weight_rows": Nw,
                    "rot_block": wl.rot_block,
                    "path": wl.kind + ("-unfused" if unfused else "") + ("-single-call" if single else "")
-                   + (f"-{args.path}-rot{args.rot_out}" if quantout or then_quant else ""),
+                   + (f"-{args.path}-rot{args.rot_out}" if quantout else ""),
                    "parallelism": "single GPU",
-                   "operand_copies": copies},
+                   "operand_copies": copies, "clock_ramp_steps": ramp},
         "pct_of_peak": 100.0 * ops / (ms_per_step * 1e-3) / (peak * 1e12),
         "roofline": {"bound": "mfma", "achieved": ops / tg / 1e12, "peak": peak, "unit": "TFLOP/s",
                      "frac": ops / tg / 1e12 / peak, "traffic": traffic,
@@ -462,22 +471,14 @@ def main():
                          "avg_launch_us": tsw * 1e6, "algorithmic_bytes": sw_bytes}
         out["roofline"]["kernel"] = "gemm_tile (GEMM + dequant epilogue onto 2N columns)"
     if quantout:
-        trq = avg(2)
-        rq_bytes = 2 * M * n_out + 4 * M * nblk + 4 * M           # codes read + written, amax, scales
-        out["requantize"] = {"bound": "hbm", "achieved": rq_bytes / trq / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": rq_bytes / trq / 1e9 / PEAK_HBM_GBS,
-                             "avg_launch_us": trq * 1e6, "algorithmic_bytes": rq_bytes}
-        out["roofline"]["kernel"] = ("gemm_tile (GEMM + SwiGLU epilogue quantizing 128-column blocks "
-                                     "for the next linear)")
-    if then_quant:
         th = avg(2)
         qh_bytes = 2 * M * n_out + M * n_out + 4 * M
         out["quantizer_h"] = {"bound": "hbm", "achieved": qh_bytes / th / 1e9, "peak": PEAK_HBM_GBS,
                               "unit": "GB/s", "frac": qh_bytes / th / 1e9 / PEAK_HBM_GBS,
                               "avg_launch_us": th * 1e6, "algorithmic_bytes": qh_bytes}
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, inp, unfused,
-                                           args.rot_out if (quantout or then_quant) else None)
+        out["cpu_baseline"] = cpu_baseline(wl, inp, unfused, args.rot_out if quantout else None)
+    out["context_h100"] = H100_CONTEXT
     print(json.dumps(out), flush=True)
 
 

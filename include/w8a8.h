@@ -128,9 +128,14 @@ w8a8_status w8a8_quantize_act_fp8_packed(const uint16_t* x, int64_t M, int64_t K
                                          uint8_t* q_packed, float* s_tok, hipStream_t stream);
 
 /* ---- stage 2 alone: acc[m][n] = sum_k q[m][k] * w[n][k], exact int32 ----------
- * The raw integer contraction (diagnostic / test entry point). acc is int32 [M, N]. */
+ * The raw integer contraction (diagnostic / test entry point). acc is int32 [M, N].
+ * The _packed form takes both code matrices in the packed layout (q_packed of M
+ * rows, w_packed of N rows) and runs the same kernel, tile choice and K loop as
+ * w8a8_gemm_dequant_packed, so it exposes the accumulators that epilogue sees. */
 w8a8_status w8a8_gemm_i32(const int8_t* q, const int8_t* w, int32_t* acc,
                           int64_t M, int64_t N, int64_t K, hipStream_t stream);
+w8a8_status w8a8_gemm_i32_packed(const int8_t* q_packed, const int8_t* w_packed, int32_t* acc,
+                                 int64_t M, int64_t N, int64_t K, hipStream_t stream);
 
 /* ---- stages 2+3: integer GEMM with the fused dequant epilogue ---------------
  * y[m][n] = bf16( acc[m][n] * s_tok[m] * s_ch[n] + bias[n] ), computed from the
@@ -228,70 +233,32 @@ w8a8_status w8a8_fp8_linear_packed(const uint16_t* x, const uint8_t* w_packed, c
                                    hipStream_t stream);
 
 /* ---- gate/up SwiGLU whose output is quantized for the next linear -----------
- * The down projection that follows the gate/up pair quantizes its input (the
- * SwiGLU output h [M, N]) per token, optionally after the block-128 rotation,
- * exactly as w8a8_quantize_act does (INT8 ConvRot card, latency-table notes).
- * These calls produce that input -- int8 codes in the packed layout plus the
- * per-token scales -- without writing h: the gate/up GEMM's epilogue quantizes
- * each 128-column block of h on its own scale (one GEMM tile covers exactly
- * one block), then a light pass rescales the blocks to the row scale.  The
- * pages do not describe this fusion; its definition:
- *   block b of row m (columns 128b .. 128b+127, rotated when rot_out == 128):
- *     amax_b = max|y|, s_b = fl32(amax_b / 127), q_b = round-half-even(y / s_b);
- *   s_tok[m] = fl32(max_b amax_b / 127)  -- equal to w8a8_quantize_act's scale;
- *   q = round-half-even(fl32(q_b * fl32(s_b / s_tok[m])))  (0 if s_tok[m] == 0).
- * Codes of the block holding the row's amax equal w8a8_quantize_act's; the
- * others may differ from them by one step (a second rounding).
- * Shapes: the gate/up GEMM's (K % 128 == 0, N % 8 == 0) and N % 64 == 0;
- * rot_out == 128 needs N % 128 == 0.  Codes are w8a8_packed_bytes(M, N) bytes in
- * the packed layout of a [M, N] activation (padding rows untouched): the A
- * operand of w8a8_gemm_dequant_packed for the down projection (K = N). */
-
-/* Bytes of the block amax array [M, ceil(N / 128)] fp32 (0 for M or N <= 0). */
-size_t w8a8_block_amax_bytes(int64_t M, int64_t N);
+ * The down projection that follows the gate/up pair is an INT8 projection too,
+ * so its input -- the SwiGLU output h [M, N] -- goes through the same per-token
+ * activation quantizer as every INT8 projection's input (INT8 ConvRot card,
+ * notes under the latency table), after the paired gate/up epilogue ("Loading
+ * CLEF INT8", fuse_mlp):
+ *   h = bf16(silu(g) * u)                    as w8a8_gateup_swiglu_packed;
+ *   q_packed, s_tok = w8a8_quantize_act_packed(h, rot_out)   bit for bit.
+ * Three kernels on `stream`: the quantizer of x (rotation rot_in), the gate/up
+ * GEMM with the SwiGLU epilogue writing h into the workspace, the quantizer of
+ * h.  The codes are w8a8_packed_bytes(M, N) bytes in the packed layout of a
+ * [M, N] activation (padding rows untouched): the A operand of
+ * w8a8_gemm_dequant_packed for the down projection (its K = N); s_tok is [M].
+ * Shapes: the gate/up GEMM's (K % 128 == 0) and N % 64 == 0, N <= W8A8_MAX_K;
+ * rot_out == 128 needs N % 128 == 0; rot_in and rot_out are 0 or 128
+ * (W8A8_ERR_BAD_ARGUMENT otherwise). */
 
 /* Workspace of w8a8_gateup_swiglu_quant_packed: w8a8_workspace_bytes(M, K)
- * followed by the block amax array on a 256-byte boundary. */
+ * (the codes and scales of x) followed by h, bf16 [M, N], on a 256-byte
+ * boundary.  Afterwards it holds those values.  0 for M, N or K <= 0. */
 size_t w8a8_swiglu_quant_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
-/* First step alone: packed x codes + s_tok and the packed [2N, K] gate/up
- * weight as for w8a8_gemm_swiglu_packed; writes the block codes (codes_packed)
- * and block_amax [M, ceil(N / 128)] (row-major), and, when h is not NULL, the
- * bf16 SwiGLU output [M, N] that was quantized. */
-w8a8_status w8a8_gemm_swiglu_blockquant_packed(const int8_t* q_packed, const float* s_tok,
-                                              const int8_t* w_gateup_packed, const float* s_ch,
-                                              const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                              int rot_out, int8_t* codes_packed, float* block_amax,
-                                              uint16_t* h, hipStream_t stream);
-
-/* Second step alone: rescales block codes (packed [M, N], rewritten in place)
- * to the row scale and writes s_tok [M].  N % 64 == 0. */
-w8a8_status w8a8_requantize_blocks_packed(int8_t* codes_packed, const float* block_amax, int64_t M,
-                                          int64_t N, float* s_tok, hipStream_t stream);
-
-/* Whole: quantize x (rotation rot_in), gate/up GEMM with the block-quantizing
- * epilogue (rotation rot_out), rescale -> q_packed, s_tok.  Three kernels on
- * `stream`; `workspace` holds w8a8_swiglu_quant_workspace_bytes(M, N, K)
- * bytes, caller-owned. */
 w8a8_status w8a8_gateup_swiglu_quant_packed(const uint16_t* x, const int8_t* w_gateup_packed,
                                             const float* s_ch, const uint16_t* bias, int64_t M,
                                             int64_t N, int64_t K, int rot_in, int rot_out,
                                             int8_t* q_packed, float* s_tok, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream);
-
-/* ---- measurement aid (not a step of the path; no page describes it) ---------
- * The rate the matrix cores sustain with operands in registers and no memory
- * traffic: the ceiling the GEMM's MFMA rate is measured against at the clock
- * the chip holds under load.  Launches `blocks` workgroups of 4 waves; each
- * wave runs `iters` rounds of four independent MFMAs -- kind 0: int8
- * 32x32x32 (65,536 ops each), kind 1: bf16 32x32x16 (32,768 flops each, the
- * instruction the E4M3FN GEMM runs on) -- alternating between two fixed
- * operand patterns of the lane index, and stores each lane's accumulator sum
- * (int32, wrapping) in sink [blocks * 256] (caller-owned, 16-byte aligned).
- * Ops per launch: blocks * 4 * iters * 4 * (65,536 or 32,768).
- * 1 <= iters <= 2^40, 1 <= blocks <= 65,536; kind outside {0, 1} is
- * W8A8_ERR_BAD_ARGUMENT. */
-w8a8_status w8a8_mfma_probe(int kind, int64_t iters, int blocks, int32_t* sink, hipStream_t stream);
 
 #ifdef __cplusplus
 }

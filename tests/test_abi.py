@@ -33,6 +33,7 @@ def lib():
         "w8a8_quantize_act": (I, [P, I64, I64, I, P, P, P]),
         "w8a8_quantize_act_fp8": (I, [P, I64, I64, I, P, P, P]),
         "w8a8_gemm_i32": (I, [P, P, P, I64, I64, I64, P]),
+        "w8a8_gemm_i32_packed": (I, [P, P, P, I64, I64, I64, P]),
         "w8a8_gemm_dequant": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
         "w8a8_gemm_swiglu": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
         "w8a8_fp8_gemm_dequant": (I, [P, P, P, P, P, P, I64, I64, I64, P]),
@@ -50,12 +51,8 @@ def lib():
         "w8a8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_gateup_swiglu_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_fp8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
-        "w8a8_block_amax_bytes": (SZ, [I64, I64]),
         "w8a8_swiglu_quant_workspace_bytes": (SZ, [I64, I64, I64]),
-        "w8a8_gemm_swiglu_blockquant_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, P, P, P]),
-        "w8a8_requantize_blocks_packed": (I, [P, P, I64, I64, P, P]),
         "w8a8_gateup_swiglu_quant_packed": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
-        "w8a8_mfma_probe": (I, [I, I64, I, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -76,10 +73,19 @@ def test_header_declares_the_documented_entry_points():
             "w8a8_packed_bytes", "w8a8_pack_weight", "w8a8_linear_packed",
             "w8a8_gateup_swiglu_packed", "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed",
             "w8a8_quantize_act_fp8_packed", "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed",
-            "w8a8_fp8_gemm_dequant_packed", "w8a8_swiglu", "w8a8_block_amax_bytes",
-            "w8a8_swiglu_quant_workspace_bytes", "w8a8_gemm_swiglu_blockquant_packed",
-            "w8a8_requantize_blocks_packed", "w8a8_gateup_swiglu_quant_packed"}
+            "w8a8_fp8_gemm_dequant_packed", "w8a8_swiglu", "w8a8_swiglu_quant_workspace_bytes",
+            "w8a8_gateup_swiglu_quant_packed", "w8a8_gemm_i32_packed"}
     assert want <= set(declared_symbols())
+
+
+def test_measurement_aids_are_not_in_the_library():
+    """The MFMA rate and fp8-accuracy probes live in the bench-only probe library."""
+    import subprocess
+    syms = subprocess.run(["nm", "-D", "--defined-only", str(LIB)], capture_output=True, text=True).stdout
+    assert "w8a8_" in syms and "probe" not in syms
+    probe = ROOT / "w8a8_quantized_linear_amd" / "probe" / "libw8a8_probe.so"
+    psyms = subprocess.run(["nm", "-D", "--defined-only", str(probe)], capture_output=True, text=True).stdout
+    assert "w8a8_probe_mfma_rate" in psyms and "w8a8_probe_fp8_contraction" in psyms
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -201,36 +207,33 @@ def test_pack_weight_argument_checks(lib):
 
 
 def test_swiglu_quant_sizes_and_argument_checks(lib):
-    assert lib.w8a8_block_amax_bytes(0, 128) == 0
-    assert lib.w8a8_block_amax_bytes(3, 320) == 3 * 3 * 4          # ceil(320 / 128) blocks
-    assert lib.w8a8_block_amax_bytes(2270, 17408) == 2270 * 136 * 4
     ws = lib.w8a8_swiglu_quant_workspace_bytes(4, 256, 512)
-    assert ws == lib.w8a8_workspace_bytes(4, 512) + 256             # 4 x 2 amax, padded to 256
+    assert ws == lib.w8a8_workspace_bytes(4, 512) + 4 * 256 * 2     # x codes + scales, then bf16 h
+    assert lib.w8a8_swiglu_quant_workspace_bytes(3, 192, 512) == lib.w8a8_workspace_bytes(3, 512) + 1280
     assert lib.w8a8_swiglu_quant_workspace_bytes(0, 256, 512) == 0
-    b = lib.w8a8_gemm_swiglu_blockquant_packed
-    assert b(None, A, A, A, None, 4, 256, 512, 0, A, A, None, None) == NULLP
-    assert b(A, A, A, A, None, 4, 256, 512, 0, None, A, None, None) == NULLP
-    assert b(A, A, A, A, None, 4, 256, 512, 0, A, None, None, None) == NULLP
-    assert b(A, A, A, A, None, 4, 200, 512, 0, A, A, None, None) == SHAPE      # N % 64
-    assert b(A, A, A, A, None, 4, 320, 512, 128, A, A, None, None) == SHAPE    # rotation: N % 128
-    assert b(A, A, A, A, None, 4, 256, 512, 64, A, A, None, None) == BADARG    # rot_out
-    assert b(A, A, A, A, None, 4, 256, 320, 0, A, A, None, None) == SHAPE      # K % 128
-    assert b(A, A, A, A, None, 4, 256, 512, 0, A, A, U, None) == MISALIGNED    # h
-    assert b(None, None, None, None, None, 0, 256, 512, 0, None, None, None, None) == OK
-    r = lib.w8a8_requantize_blocks_packed
-    assert r(None, A, 4, 256, A, None) == NULLP
-    assert r(A, A, 4, 256, None, None) == NULLP
-    assert r(A, A, 4, 96, A, None) == SHAPE
-    assert r(A, A, -1, 256, A, None) == SHAPE
-    assert r(U, A, 4, 256, A, None) == MISALIGNED
-    assert r(None, None, 0, 256, None, None) == OK
     g = lib.w8a8_gateup_swiglu_quant_packed
     assert g(A, A, A, None, 4, 256, 512, 0, 128, A, A, A, ws - 1, None) == BADARG
     assert g(A, A, A, None, 4, 256, 512, 3, 128, A, A, A, ws, None) == BADARG   # rot_in
+    assert g(A, A, A, None, 4, 256, 512, 0, 64, A, A, A, ws, None) == BADARG    # rot_out
     assert g(A, A, A, None, 4, 256, 512, 0, 128, None, A, A, ws, None) == NULLP
+    assert g(A, A, A, None, 4, 256, 512, 0, 128, A, None, A, ws, None) == NULLP
     assert g(A, A, A, None, 4, 256, 512, 0, 128, A, A, U, ws, None) == MISALIGNED
+    assert g(A, A, A, U, 4, 256, 512, 0, 128, A, A, A, ws, None) == MISALIGNED  # bias
     assert g(A, A, A, None, 4, 192, 512, 0, 128, A, A, A, ws, None) == SHAPE    # rotation: N % 128
+    assert g(A, A, A, None, 4, 200, 512, 0, 0, A, A, A, ws, None) == SHAPE      # N % 64
+    assert g(A, A, A, None, 4, 256, 320, 0, 0, A, A, A, ws, None) == SHAPE      # K % 128
+    assert g(A, A, A, None, 4, 131072 + 128, 512, 0, 0, A, A, A, 1 << 40, None) == SHAPE  # N too long
     assert g(None, None, None, None, 0, 256, 512, 0, 0, None, None, None, 0, None) == OK
+
+
+def test_packed_i32_argument_checks(lib):
+    g = lib.w8a8_gemm_i32_packed
+    assert g(None, A, A, 4, 8, 128, None) == NULLP
+    assert g(A, A, None, 4, 8, 128, None) == NULLP
+    assert g(A, A, A, 4, 8, 64, None) == SHAPE
+    assert g(A, A, A, 4, 12, 128, None) == SHAPE
+    assert g(A, U, A, 4, 8, 128, None) == MISALIGNED
+    assert g(A, A, A, 0, 8, 128, None) == OK
 
 
 def test_valid_call_without_gpu_reports_device(lib):
@@ -240,21 +243,24 @@ def test_valid_call_without_gpu_reports_device(lib):
     assert lib.w8a8_quantize_act(A, 4, 128, 0, A, A, None) == DEVICE
     assert lib.w8a8_gemm_i32(A, A, A, 4, 8, 128, None) == DEVICE
     assert lib.w8a8_pack_weight(A, 4, 128, A, None) == DEVICE
-    assert lib.w8a8_requantize_blocks_packed(A, A, 4, 256, A, None) == DEVICE
-    assert lib.w8a8_gemm_swiglu_blockquant_packed(A, A, A, A, None, 4, 256, 512, 128, A, A, None,
-                                                  None) == DEVICE
+    assert lib.w8a8_gemm_i32_packed(A, A, A, 4, 8, 128, None) == DEVICE
+    ws = lib.w8a8_swiglu_quant_workspace_bytes(4, 256, 512)
+    assert lib.w8a8_gateup_swiglu_quant_packed(A, A, A, None, 4, 256, 512, 0, 128, A, A, A, ws, None) == DEVICE
 
 
-def test_mfma_probe_argument_checks(lib):
-    p = lib.w8a8_mfma_probe
-    assert p(2, 10, 1, A, None) == BADARG          # kind
-    assert p(-1, 10, 1, A, None) == BADARG
-    assert p(0, 0, 1, A, None) == SHAPE            # iters
-    assert p(0, (1 << 40) + 1, 1, A, None) == SHAPE
-    assert p(1, 10, 0, A, None) == SHAPE           # blocks
-    assert p(1, 10, 65537, A, None) == SHAPE
-    assert p(0, 10, 1, None, None) == NULLP
-    assert p(0, 10, 1, A + 4, None) == MISALIGNED
-    import torch
-    if not torch.cuda.is_available():
-        assert p(0, 10, 1, A, None) == DEVICE
+def test_probe_argument_checks():
+    """The bench-only probes refuse bad arguments before launching anything."""
+    probe = ROOT / "w8a8_quantized_linear_amd" / "probe" / "libw8a8_probe.so"
+    pl = ctypes.CDLL(str(probe))
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    pl.w8a8_probe_mfma_rate.restype, pl.w8a8_probe_mfma_rate.argtypes = I, [I, I64, I, P, P]
+    r = pl.w8a8_probe_mfma_rate
+    assert r(2, 10, 1, A, None) == -1 and r(0, 0, 1, A, None) == -1 and r(1, 10, 0, A, None) == -1
+    assert r(0, 10, 1, None, None) == -1 and r(0, (1 << 40) + 1, 1, A, None) == -1
+    pl.w8a8_probe_fp8_contraction.restype = I
+    pl.w8a8_probe_fp8_contraction.argtypes = [I, P, P, P, I64, I64, I64, P]
+    c = pl.w8a8_probe_fp8_contraction
+    assert c(0, A, A, A, 33, 32, 64, None) == -1      # M % 32
+    assert c(0, A, A, A, 32, 32, 96, None) == -1      # K % 64
+    assert c(5, A, A, A, 32, 32, 64, None) == -1      # kind
+    assert c(0, None, A, A, 32, 32, 64, None) == -1

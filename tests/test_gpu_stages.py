@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as W
-from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, say)
+from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, sample_rows, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -91,6 +91,51 @@ def test_gemm_i32_exact(lib, orc, M, N, K):
     torch.cuda.synchronize()
     ref = orc.gemm_i32(q.numpy(), w.numpy())
     assert np.array_equal(acc.cpu().numpy(), ref)
+
+
+def _tile_choice(M, N):
+    """The launcher's tile choice for an (unpaired) GEMM of M tokens x N weight rows:
+    the least ceil(tiles / 256) * tile area / efficiency over 256x256 (1.0), 192x128
+    (0.9) and 128x128 (0.8), ties to the larger tile."""
+    def cost(bm, bn, eff):
+        tiles = -(-M // bm) * -(-N // bn)
+        return -(-tiles // 256) * bm * bn / eff
+    c256, c192, c128 = cost(256, 256, 1.0), cost(192, 128, 0.9), cost(128, 128, 0.8)
+    if c256 <= c192 and c256 <= c128:
+        return "256x256"
+    return "192x128" if c192 <= c128 else "128x128"
+
+
+# One shape per tile the launcher picks, at the workloads' depths (K = 5,120 and
+# 17,408: long K loops over the 4-stage ring), in both operand layouts.
+TILE_SHAPES = [(300, 264, 512, "128x128"), (1502, 4096, 5120, "192x128"), (2048, 8192, 17408, "256x256")]
+
+
+@pytest.mark.parametrize("packed", [False, True], ids=["row-major", "packed"])
+@pytest.mark.parametrize("M,N,K,tile", TILE_SHAPES, ids=[t[3] for t in TILE_SHAPES])
+def test_gemm_i32_exact_on_every_tile(lib, orc, M, N, K, tile, packed):
+    """int32 accumulators bit for bit against the oracle's integer GEMM, on the tile
+    shapes and K loops the workloads run (the dequant and SwiGLU epilogues read exactly
+    these accumulators)."""
+    assert _tile_choice(M, N) == tile
+    say(f"gemm_i32 {'packed' if packed else 'row-major'} M={M} N={N} K={K} ({tile} tiles)")
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(M + N + K)
+    q = torch.randint(-127, 128, (M, K), generator=g, device=dev, dtype=torch.int32).to(torch.int8)
+    w = torch.randint(-127, 128, (N, K), generator=g, device=dev, dtype=torch.int32).to(torch.int8)
+    q[1] = 127                            # extreme rows: |acc| up to 127^2 K
+    w[2] = -127
+    q[M - 1, ::2] = -127
+    if packed:
+        acc = lib.w8a8_gemm_i32_packed(lib.w8a8_pack_weight(q), lib.w8a8_pack_weight(w), M, N, K)
+    else:
+        acc = lib.w8a8_gemm_i32(q, w)
+    torch.cuda.synchronize()
+    rows = sample_rows(M, n=16, seed=K, tile=256 if tile == "256x256" else 128) if M > 300 else np.arange(M)
+    got = acc.cpu().numpy()[rows]
+    ref = orc.gemm_i32(np.ascontiguousarray(q.cpu().numpy()[rows]), w.cpu().numpy())
+    assert np.array_equal(got, ref), f"{np.count_nonzero(got != ref)} accumulators differ"
+    assert int(acc[1, 2]) == -16129 * K
 
 
 def test_gemm_i32_extremes(lib, orc):

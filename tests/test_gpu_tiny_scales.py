@@ -7,8 +7,8 @@ range, so a row whose scale is below 2^-90 is multiplied, values and scale, by
 row scales on both sides of that threshold and down to the smallest subnormals,
 and require the codes and scales to equal the oracle's (IEEE division) bit for
 bit: the int8 and E4M3FN quantizers (row-major and packed, rotation on and off),
-the single-launch short path's workspace codes, and the block quantizer in the
-gate/up epilogue.
+the single-launch short path's workspace codes, and the quantizer of the gate/up
+SwiGLU output for the next linear.
 """
 import numpy as np
 import pytest
@@ -97,26 +97,26 @@ def test_short_path_on_tiny_rows(lib, orc, rot):
 
 
 @pytest.mark.parametrize("shift", [38, 44, 50, 56])
-def test_block_quantizer_on_tiny_swiglu_output(lib, orc, shift):
-    """Per-channel weight scales times 2^-shift make the SwiGLU output ~2^(-2 shift):
-    block scales from ~2^-80 down to subnormal-range blocks."""
+def test_swiglu_output_quantizer_on_tiny_values(lib, orc, shift):
+    """Per-channel weight scales times 2^-shift make the SwiGLU output ~2^(-2 shift), so
+    the row scales of its per-token quantization run from ~2^-80 down into the
+    subnormal range: codes and scales equal the oracle's quantizer applied to the
+    kernel's own SwiGLU output, bit for bit."""
     M, K, N, rot_out = 70, 256, 384, 128
-    say(f"tiny SwiGLU output, block quantizer, scales x 2^-{shift}")
+    say(f"tiny SwiGLU output, quantized for the next linear, scales x 2^-{shift}")
     wl = W.custom("gateup", M, K, N, 0, bias=False, seed=shift)
     inp = W.make_inputs(wl)
     dev = torch.device("cuda")
     wq, s_ch = orc.quantize_i8(W.bits(inp.w), 0)
     s_ch = (s_ch.astype(np.float64) * 2.0 ** -shift).astype(np.float32)
     wp = lib.w8a8_pack_weight(torch.from_numpy(wq).to(dev))
-    qx, sx = orc.quantize_i8(W.bits(inp.x), 0)
-    qx_p = lib.w8a8_pack_weight(torch.from_numpy(qx).to(dev))
-    codes, amax, h = lib.w8a8_gemm_swiglu_blockquant_packed(qx_p, torch.from_numpy(sx).to(dev), wp,
-                                                             torch.from_numpy(s_ch).to(dev), K, bias=None,
-                                                             rot_out=rot_out, want_h=True)
+    ws = torch.empty(lib.swiglu_quant_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+    q, s = lib.w8a8_gateup_swiglu_quant_packed(inp.x.to(dev), wp, N, torch.from_numpy(s_ch).to(dev), None,
+                                               rot_in=0, rot_out=rot_out, workspace=ws)
     torch.cuda.synchronize()
-    h_gpu = bf16_bits(h)
-    qb_ref, amax_ref = orc.block_quantize(h_gpu, rot_out)
-    say(f"  block amax from {float(np.min(amax_ref[amax_ref > 0])):.3e} to {float(np.max(amax_ref)):.3e}")
-    qb = _unpack(codes.cpu().numpy(), M, N)
-    assert np.array_equal(qb, qb_ref), f"block codes: {np.count_nonzero(qb != qb_ref)} differ"
-    assert np.array_equal(amax.cpu().numpy().view(np.uint32), amax_ref.view(np.uint32)), "block amax"
+    h_gpu = bf16_bits(lib.swiglu_quant_h(ws, M, N, K))
+    q_ref, s_ref = orc.quantize_i8(h_gpu, rot_out)
+    say(f"  row scales from {float(np.min(s_ref[s_ref > 0])):.3e} to {float(np.max(s_ref)):.3e}")
+    got = _unpack(q.cpu().numpy(), M, N).view(np.int8)
+    assert np.array_equal(got, q_ref), f"codes: {np.count_nonzero(got != q_ref)} differ"
+    assert np.array_equal(s.cpu().numpy().view(np.uint32), s_ref.view(np.uint32)), "scales"

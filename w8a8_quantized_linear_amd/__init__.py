@@ -28,9 +28,8 @@ __all__ = [
     "w8a8_gateup_swiglu", "w8a8_fp8_linear", "w8a8_linear_packed", "w8a8_gateup_swiglu_packed",
     "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed", "w8a8_quantize_act_fp8_packed",
     "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed", "w8a8_fp8_gemm_dequant_packed",
-    "w8a8_swiglu", "block_amax_bytes", "swiglu_quant_workspace_bytes",
-    "w8a8_gemm_swiglu_blockquant_packed", "w8a8_requantize_blocks_packed",
-    "w8a8_gateup_swiglu_quant_packed",
+    "w8a8_swiglu", "swiglu_quant_workspace_bytes", "w8a8_gateup_swiglu_quant_packed",
+    "w8a8_gemm_i32_packed", "swiglu_quant_h",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
@@ -49,6 +48,7 @@ _SIGS = {
     "w8a8_quantize_act": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "w8a8_quantize_act_fp8": (_I, [_P, _I64, _I64, _I, _P, _P, _P]),
     "w8a8_gemm_i32": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
+    "w8a8_gemm_i32_packed": (_I, [_P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_dequant": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_gemm_swiglu": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
     "w8a8_fp8_gemm_dequant": (_I, [_P, _P, _P, _P, _P, _P, _I64, _I64, _I64, _P]),
@@ -64,12 +64,8 @@ _SIGS = {
     "w8a8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_gateup_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_fp8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
-    "w8a8_block_amax_bytes": (_SZ, [_I64, _I64]),
     "w8a8_swiglu_quant_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
-    "w8a8_gemm_swiglu_blockquant_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _P, _P, _P]),
-    "w8a8_requantize_blocks_packed": (_I, [_P, _P, _I64, _I64, _P, _P]),
     "w8a8_gateup_swiglu_quant_packed": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
-    "w8a8_mfma_probe": (_I, [_I, _I64, _I, _P, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -96,15 +92,59 @@ def _stream():
     return torch.cuda.current_stream().cuda_stream
 
 
+def _device_ok(t: torch.Tensor, name: str) -> None:
+    """The library runs on the current HIP device and torch's current stream there."""
+    if not t.is_cuda:
+        raise ValueError(f"{name}: must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name}: is on {t.device}, but the current device is "
+                         f"cuda:{torch.cuda.current_device()}")
+
+
 def _want(t: torch.Tensor, dtype: torch.dtype, name: str, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
     if t.dtype != dtype:
         raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
     if t.dim() != ndim:
         raise ValueError(f"{name}: expected {ndim} dims, got {tuple(t.shape)}")
-    if not t.is_cuda:
-        raise ValueError(f"{name}: must be a device tensor")
+    _device_ok(t, name)
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+
+
+def _out(t: Optional[torch.Tensor], dtype: torch.dtype, numel: int, name: str, dev: torch.device,
+         shape=None) -> torch.Tensor:
+    """A caller-supplied output (checked: dtype, device, contiguity, at least `numel`
+    elements, and `shape` when given), or a new tensor of `shape` (or `numel`
+    elements, at least one)."""
+    if t is None:
+        return torch.empty(shape if shape is not None else (max(numel, 1),), dtype=dtype, device=dev)
+    _want(t, dtype, name, t.dim())
+    if t.device != dev:
+        raise ValueError(f"{name}: is on {t.device}, the inputs on {dev}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.numel() < numel:
+        raise ValueError(f"{name}: needs at least {numel} elements, has {t.numel()}")
+    return t
+
+
+def _workspace(t: Optional[torch.Tensor], need: int, dev: torch.device) -> torch.Tensor:
+    """Caller-supplied workspace (a contiguous device tensor of at least `need` bytes,
+    any dtype) or a new uint8 one."""
+    if t is None:
+        return torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("workspace: expected a torch.Tensor")
+    _device_ok(t, "workspace")
+    if t.device != dev:
+        raise ValueError(f"workspace: is on {t.device}, the inputs on {dev}")
+    if not t.is_contiguous():
+        raise ValueError("workspace: must be contiguous")
+    if t.numel() * t.element_size() < need:
+        raise ValueError(f"workspace: needs {need} bytes, has {t.numel() * t.element_size()}")
+    return t
 
 
 def workspace_bytes(M: int, K: int) -> int:
@@ -132,9 +172,7 @@ def w8a8_pack_weight(w: torch.Tensor, out: Optional[torch.Tensor] = None) -> tor
     _want(w, w.dtype, "w", 2)
     rows, K = w.shape
     n = packed_bytes(rows, K)
-    wp = out if out is not None else torch.empty((max(n, 1),), dtype=w.dtype, device=w.device)
-    if wp.numel() < n:
-        raise ValueError("out is smaller than packed_bytes(rows, K)")
+    wp = _out(out, w.dtype, n, "out", w.device)
     _check(_lib.w8a8_pack_weight(_ptr(w), rows, K, _ptr(wp), _stream()), "w8a8_pack_weight")
     return wp
 
@@ -145,8 +183,9 @@ def w8a8_quantize_act(x: torch.Tensor, rot_block: int = 0,
     """Per-row int8 quantizer: x bf16 [M, K] -> (q int8 [M, K], s fp32 [M])."""
     _want(x, torch.bfloat16, "x", 2)
     M, K = x.shape
-    q, s = out if out is not None else (torch.empty((M, K), dtype=torch.int8, device=x.device),
-                                        torch.empty((M,), dtype=torch.float32, device=x.device))
+    q0, s0 = out if out is not None else (None, None)
+    q = _out(q0, torch.int8, M * K, "q", x.device, shape=(M, K))
+    s = _out(s0, torch.float32, M, "s", x.device, shape=(M,))
     _check(_lib.w8a8_quantize_act(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()),
            "w8a8_quantize_act")
     return q, s
@@ -157,8 +196,9 @@ def w8a8_quantize_act_fp8(x: torch.Tensor, rot_block: int = 0,
     """Per-row E4M3FN quantizer: x bf16 [M, K] -> (codes uint8 [M, K], s fp32 [M])."""
     _want(x, torch.bfloat16, "x", 2)
     M, K = x.shape
-    q, s = out if out is not None else (torch.empty((M, K), dtype=torch.uint8, device=x.device),
-                                        torch.empty((M,), dtype=torch.float32, device=x.device))
+    q0, s0 = out if out is not None else (None, None)
+    q = _out(q0, torch.uint8, M * K, "q", x.device, shape=(M, K))
+    s = _out(s0, torch.float32, M, "s", x.device, shape=(M,))
     _check(_lib.w8a8_quantize_act_fp8(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()),
            "w8a8_quantize_act_fp8")
     return q, s
@@ -168,10 +208,9 @@ def _quant_packed(fname, x, rot_block, qdtype, out):
     _want(x, torch.bfloat16, "x", 2)
     M, K = x.shape
     n = packed_bytes(M, K)
-    q, s = out if out is not None else (torch.empty((max(n, 1),), dtype=qdtype, device=x.device),
-                                        torch.empty((M,), dtype=torch.float32, device=x.device))
-    if q.numel() < n:
-        raise ValueError("q is smaller than packed_bytes(M, K)")
+    q0, s0 = out if out is not None else (None, None)
+    q = _out(q0, qdtype, n, "q", x.device)
+    s = _out(s0, torch.float32, M, "s", x.device, shape=(M,))
     _check(getattr(_lib, fname)(_ptr(x), M, K, rot_block, _ptr(q), _ptr(s), _stream()), fname)
     return q, s
 
@@ -195,8 +234,22 @@ def w8a8_gemm_i32(q: torch.Tensor, w: torch.Tensor, out: Optional[torch.Tensor] 
     N = w.shape[0]
     if w.shape[1] != K:
         raise ValueError("q and w disagree on K")
-    acc = out if out is not None else torch.empty((M, N), dtype=torch.int32, device=q.device)
+    acc = _out(out, torch.int32, M * N, "out", q.device, shape=(M, N))
     _check(_lib.w8a8_gemm_i32(_ptr(q), _ptr(w), _ptr(acc), M, N, K, _stream()), "w8a8_gemm_i32")
+    return acc
+
+
+def w8a8_gemm_i32_packed(q_packed: torch.Tensor, w_packed: torch.Tensor, M: int, N: int, K: int,
+                         out: Optional[torch.Tensor] = None):
+    """acc int32 [M, N] from packed int8 codes (q_packed of M rows, w_packed of N rows):
+    the accumulators of the packed GEMM that the whole paths run."""
+    _want(q_packed, torch.int8, "q_packed", 1)
+    _want(w_packed, torch.int8, "w_packed", 1)
+    if q_packed.numel() < packed_bytes(M, K) or w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("packed operands smaller than packed_bytes(rows, K)")
+    acc = _out(out, torch.int32, M * N, "out", q_packed.device, shape=(M, N))
+    _check(_lib.w8a8_gemm_i32_packed(_ptr(q_packed), _ptr(w_packed), _ptr(acc), M, N, K, _stream()),
+           "w8a8_gemm_i32_packed")
     return acc
 
 
@@ -212,7 +265,7 @@ def _epi(fname, q, s_tok, w, s_ch, bias, n_out, qdtype, out):
         raise ValueError("inconsistent shapes")
     if bias is not None and bias.shape[0] != w.shape[0]:
         raise ValueError("bias length must equal the weight's rows")
-    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=q.device)
+    y = _out(out, torch.bfloat16, M * n_out, "out", q.device, shape=(M, n_out))
     _check(getattr(_lib, fname)(_ptr(q), _ptr(s_tok), _ptr(w), _ptr(s_ch), _ptr(bias), _ptr(y),
                                 M, n_out, K, _stream()), fname)
     return y
@@ -248,7 +301,7 @@ def _epi_packed(fname, q, s_tok, w, s_ch, bias, M, n_out, K, qdtype, out):
         raise ValueError("inconsistent shapes")
     if bias is not None and bias.shape[0] != rows:
         raise ValueError("bias length must equal the weight's rows")
-    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=q.device)
+    y = _out(out, torch.bfloat16, M * n_out, "out", q.device, shape=(M, n_out))
     _check(getattr(_lib, fname)(_ptr(q), _ptr(s_tok), _ptr(w), _ptr(s_ch), _ptr(bias), _ptr(y),
                                 M, n_out, K, _stream()), fname)
     return y
@@ -277,14 +330,17 @@ def w8a8_swiglu(gate: torch.Tensor, up: torch.Tensor, out: Optional[torch.Tensor
     """y bf16 [M, N] = silu(gate) * up for bf16 [M, N] views with the same row stride
     (e.g. the two halves of a [M, 2N] projection: h[:, :N], h[:, N:])."""
     for t, name in ((gate, "gate"), (up, "up")):
-        if t.dtype != torch.bfloat16 or t.dim() != 2 or not t.is_cuda:
+        if t.dtype != torch.bfloat16 or t.dim() != 2:
             raise ValueError(f"{name}: expected a 2-D bf16 device tensor")
+        _device_ok(t, name)
         if t.stride(1) != 1:
             raise ValueError(f"{name}: rows must be contiguous")
     if gate.shape != up.shape or gate.stride(0) != up.stride(0):
         raise ValueError("gate and up must have the same shape and row stride")
     M, N = gate.shape
-    y = out if out is not None else torch.empty((M, N), dtype=torch.bfloat16, device=gate.device)
+    if gate.device != up.device:
+        raise ValueError("gate and up must be on the same device")
+    y = _out(out, torch.bfloat16, M * N, "out", gate.device, shape=(M, N))
     _check(_lib.w8a8_swiglu(_ptr(gate), _ptr(up), gate.stride(0), _ptr(y), M, N, _stream()),
            "w8a8_swiglu")
     return y
@@ -309,12 +365,10 @@ def _path(fname, x, w, s_ch, bias, rot_block, n_out, wdtype, workspace, out, w_r
         raise ValueError("s_ch length must equal the weight's rows")
     if bias is not None and bias.shape[0] != rows:
         raise ValueError("bias length must equal the weight's rows")
-    need = workspace_bytes(M, K)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=x.device)
-    y = out if out is not None else torch.empty((M, n_out), dtype=torch.bfloat16, device=x.device)
+    ws = _workspace(workspace, workspace_bytes(M, K), x.device)
+    y = _out(out, torch.bfloat16, M * n_out, "out", x.device, shape=(M, n_out))
     _check(getattr(_lib, fname)(_ptr(x), _ptr(w), _ptr(s_ch), _ptr(bias), _ptr(y), M, n_out, K,
-                                rot_block, _ptr(workspace), workspace.numel(), _stream()), fname)
+                                rot_block, _ptr(ws), ws.numel() * ws.element_size(), _stream()), fname)
     return y
 
 
@@ -354,61 +408,23 @@ def w8a8_fp8_linear_packed(x, w_packed, N, s_ch, bias=None, rot_block=0, workspa
 
 
 # ------------------------ gate/up SwiGLU quantized for the next linear -------
-def block_amax_bytes(M: int, N: int) -> int:
-    return int(_lib.w8a8_block_amax_bytes(M, N))
-
-
 def swiglu_quant_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(_lib.w8a8_swiglu_quant_workspace_bytes(M, N, K))
 
 
-def w8a8_gemm_swiglu_blockquant_packed(q_packed, s_tok, w_gateup_packed, s_ch, K, bias=None,
-                                       rot_out=0, want_h=False, codes=None, amax=None):
-    """First step: returns (block codes, flat packed int8 [packed_bytes(M, N)];
-    block amax fp32 [M, ceil(N / 128)]; h bf16 [M, N] or None).  M = len(s_tok),
-    N = len(s_ch) / 2."""
-    _want(q_packed, torch.int8, "q_packed", 1)
-    _want(w_gateup_packed, torch.int8, "w_gateup_packed", 1)
-    _want(s_tok, torch.float32, "s_tok", 1)
-    _want(s_ch, torch.float32, "s_ch", 1)
-    if bias is not None:
-        _want(bias, torch.bfloat16, "bias", 1)
-    M, rows = s_tok.shape[0], s_ch.shape[0]
-    N = rows // 2
-    if q_packed.numel() < packed_bytes(M, K) or w_gateup_packed.numel() < packed_bytes(rows, K):
-        raise ValueError("inconsistent shapes")
-    if bias is not None and bias.shape[0] != rows:
-        raise ValueError("bias length must equal the weight's rows")
-    dev = q_packed.device
-    nblk = (N + 127) // 128
-    codes = codes if codes is not None else torch.empty((max(packed_bytes(M, N), 1),), dtype=torch.int8, device=dev)
-    amax = amax if amax is not None else torch.empty((M, nblk), dtype=torch.float32, device=dev)
-    if codes.numel() < packed_bytes(M, N) or amax.numel() < M * nblk:
-        raise ValueError("codes or amax too small")
-    h = torch.empty((M, N), dtype=torch.bfloat16, device=dev) if want_h else None
-    _check(_lib.w8a8_gemm_swiglu_blockquant_packed(_ptr(q_packed), _ptr(s_tok), _ptr(w_gateup_packed),
-                                                   _ptr(s_ch), _ptr(bias), M, N, K, rot_out, _ptr(codes),
-                                                   _ptr(amax), _ptr(h), _stream()),
-           "w8a8_gemm_swiglu_blockquant_packed")
-    return codes, amax, h
-
-
-def w8a8_requantize_blocks_packed(codes, amax, M, N, s_tok=None):
-    """Second step, in place on `codes` (flat packed int8): returns s_tok fp32 [M]."""
-    _want(codes, torch.int8, "codes", 1)
-    _want(amax, torch.float32, "amax", 2)
-    if codes.numel() < packed_bytes(M, N) or tuple(amax.shape) != (M, (N + 127) // 128):
-        raise ValueError("inconsistent shapes")
-    s = s_tok if s_tok is not None else torch.empty((M,), dtype=torch.float32, device=codes.device)
-    _check(_lib.w8a8_requantize_blocks_packed(_ptr(codes), _ptr(amax), M, N, _ptr(s), _stream()),
-           "w8a8_requantize_blocks_packed")
-    return s
+def swiglu_quant_h(workspace: torch.Tensor, M: int, N: int, K: int) -> torch.Tensor:
+    """The bf16 SwiGLU output h [M, N] that w8a8_gateup_swiglu_quant_packed leaves in its
+    workspace (a view; the workspace layout is fixed by the C header)."""
+    off = workspace_bytes(M, K)
+    raw = workspace.view(torch.uint8).reshape(-1)[off:off + 2 * M * N]
+    return raw.view(torch.bfloat16).view(M, N)
 
 
 def w8a8_gateup_swiglu_quant_packed(x, w_gateup_packed, N, s_ch, bias=None, rot_in=0, rot_out=0,
                                     workspace=None, q_out=None, s_out=None):
-    """Whole: returns (packed int8 codes [packed_bytes(M, N)], s_tok fp32 [M]) of the
-    SwiGLU output, ready as the A operand of w8a8_gemm_dequant_packed (K = N)."""
+    """Returns (packed int8 codes [packed_bytes(M, N)], s_tok fp32 [M]): the per-token
+    quantization (rotation rot_out) of the bf16 gate/up SwiGLU output, ready as the A
+    operand of w8a8_gemm_dequant_packed for the down projection (K = N)."""
     _want(x, torch.bfloat16, "x", 2)
     _want(w_gateup_packed, torch.int8, "w_gateup_packed", 1)
     _want(s_ch, torch.float32, "s_ch", 1)
@@ -420,30 +436,11 @@ def w8a8_gateup_swiglu_quant_packed(x, w_gateup_packed, N, s_ch, bias=None, rot_
     if bias is not None and bias.shape[0] != 2 * N:
         raise ValueError("bias length must equal the weight's rows")
     dev = x.device
-    need = swiglu_quant_workspace_bytes(M, N, K)
-    if workspace is None:
-        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    q = q_out if q_out is not None else torch.empty((max(packed_bytes(M, N), 1),), dtype=torch.int8, device=dev)
-    s = s_out if s_out is not None else torch.empty((M,), dtype=torch.float32, device=dev)
-    if q.numel() < packed_bytes(M, N):
-        raise ValueError("q_out too small")
+    ws = _workspace(workspace, swiglu_quant_workspace_bytes(M, N, K), dev)
+    q = _out(q_out, torch.int8, packed_bytes(M, N), "q_out", dev)
+    s = _out(s_out, torch.float32, M, "s_out", dev, shape=(M,))
     _check(_lib.w8a8_gateup_swiglu_quant_packed(_ptr(x), _ptr(w_gateup_packed), _ptr(s_ch), _ptr(bias), M, N,
-                                                K, rot_in, rot_out, _ptr(q), _ptr(s), _ptr(workspace),
-                                                workspace.numel(), _stream()),
+                                                K, rot_in, rot_out, _ptr(q), _ptr(s), _ptr(ws),
+                                                ws.numel() * ws.element_size(), _stream()),
            "w8a8_gateup_swiglu_quant_packed")
     return q, s
-
-
-# ------------------------------------------------------- measurement aid ----
-def w8a8_mfma_probe(kind: str, iters: int, blocks: int = 1024, sink: Optional[torch.Tensor] = None):
-    """MFMA-only rate probe (not a step of the path): kind "int8" (32x32x32) or "bf16"
-    (32x32x16).  Enqueues one launch on the current stream and returns the int32 sink
-    [blocks * 256] (each lane's accumulator sum)."""
-    k = {"int8": 0, "bf16": 1}[kind]
-    if sink is None:
-        sink = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
-    _want(sink, torch.int32, "sink", 1)
-    if sink.numel() < blocks * 256:
-        raise ValueError("sink: needs blocks * 256 elements")
-    _check(_lib.w8a8_mfma_probe(k, iters, blocks, _ptr(sink), _stream()), "w8a8_mfma_probe")
-    return sink

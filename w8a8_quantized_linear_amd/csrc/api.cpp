@@ -108,23 +108,15 @@ w8a8_status whole_path(w8a8::Epi epi, bool fp8, bool w_packed, const uint16_t* x
 }
 
 // The SwiGLU output quantized for the next linear: shape rules on top of the
-// gate/up GEMM's.
-w8a8_status check_swiglu_quant(int64_t M, int64_t N, int64_t K, int rot_out) {
+// gate/up GEMM's (the output rows are the next linear's activations: N % 64 == 0
+// for their packed layout, N % 128 == 0 when they are rotated).
+w8a8_status check_swiglu_quant(int64_t M, int64_t N, int64_t K, int rot_in, int rot_out) {
   w8a8_status st = check_gemm_shape(M, N, K);
   if (st != W8A8_OK) return st;
-  if (N % 64 != 0) return W8A8_ERR_BAD_SHAPE;
-  if (rot_out != 0 && rot_out != 128) return W8A8_ERR_BAD_ARGUMENT;
+  if (N % 64 != 0 || N > W8A8_MAX_K) return W8A8_ERR_BAD_SHAPE;
+  if ((rot_in != 0 && rot_in != 128) || (rot_out != 0 && rot_out != 128)) return W8A8_ERR_BAD_ARGUMENT;
   if (rot_out == 128 && N % 128 != 0) return W8A8_ERR_BAD_SHAPE;
   return W8A8_OK;
-}
-
-w8a8::QuantOut quant_out(int8_t* codes, float* amax, uint16_t* h, int rot_out) {
-  w8a8::QuantOut qo;
-  qo.codes = reinterpret_cast<uint8_t*>(codes);
-  qo.amax = amax;
-  qo.h = h;
-  qo.rot = rot_out;
-  return qo;
 }
 
 }  // namespace
@@ -154,14 +146,9 @@ size_t w8a8_workspace_bytes(int64_t M, int64_t K) {
   return align256(w8a8_packed_bytes(M, K)) + align256((size_t)M * sizeof(float));
 }
 
-size_t w8a8_block_amax_bytes(int64_t M, int64_t N) {
-  if (M <= 0 || N <= 0) return 0;
-  return (size_t)M * (size_t)((N + 127) / 128) * sizeof(float);
-}
-
 size_t w8a8_swiglu_quant_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0) return 0;
-  return w8a8_workspace_bytes(M, K) + align256(w8a8_block_amax_bytes(M, N));
+  return w8a8_workspace_bytes(M, K) + align256((size_t)M * (size_t)N * sizeof(uint16_t));
 }
 
 w8a8_status w8a8_pack_weight(const void* w, int64_t rows, int64_t K, void* w_packed,
@@ -212,6 +199,12 @@ w8a8_status w8a8_quantize_act_fp8_packed(const uint16_t* x, int64_t M, int64_t K
 w8a8_status w8a8_gemm_i32(const int8_t* q, const int8_t* w, int32_t* acc, int64_t M, int64_t N,
                           int64_t K, hipStream_t stream) {
   return gemm_epilogue(w8a8::Epi::kRawI32, false, false, q, nullptr, w, nullptr, nullptr, acc, M, N, K, stream);
+}
+
+w8a8_status w8a8_gemm_i32_packed(const int8_t* q_packed, const int8_t* w_packed, int32_t* acc, int64_t M,
+                                 int64_t N, int64_t K, hipStream_t stream) {
+  return gemm_epilogue(w8a8::Epi::kRawI32, false, true, q_packed, nullptr, w_packed, nullptr, nullptr, acc, M, N,
+                       K, stream);
 }
 
 w8a8_status w8a8_gemm_dequant(const int8_t* q, const float* s_tok, const int8_t* w, const float* s_ch,
@@ -302,47 +295,13 @@ w8a8_status w8a8_fp8_linear_packed(const uint16_t* x, const uint8_t* w_packed, c
                     workspace, workspace_bytes, stream);
 }
 
-w8a8_status w8a8_gemm_swiglu_blockquant_packed(const int8_t* q_packed, const float* s_tok,
-                                              const int8_t* w_gateup_packed, const float* s_ch,
-                                              const uint16_t* bias, int64_t M, int64_t N, int64_t K,
-                                              int rot_out, int8_t* codes_packed, float* block_amax,
-                                              uint16_t* h, hipStream_t stream) {
-  w8a8_status st = check_swiglu_quant(M, N, K, rot_out);
-  if (st != W8A8_OK) return st;
-  if (M == 0) return W8A8_OK;
-  if (!q_packed || !s_tok || !w_gateup_packed || !s_ch || !codes_packed || !block_amax)
-    return W8A8_ERR_NULL_POINTER;
-  if (!aligned16(q_packed) || !aligned16(s_tok) || !aligned16(w_gateup_packed) || !aligned16(s_ch) ||
-      !aligned16(codes_packed) || !aligned16(block_amax) || (bias && !aligned16(bias)) ||
-      (h && !aligned16(h)))
-    return W8A8_ERR_MISALIGNED;
-  if ((st = check_device()) != W8A8_OK) return st;
-  return launched(w8a8::launch_gemm_swiglu_quant(q_packed, s_tok, w_gateup_packed, s_ch, bias,
-                                                 quant_out(codes_packed, block_amax, h, rot_out), M, N, K,
-                                                 stream));
-}
-
-w8a8_status w8a8_requantize_blocks_packed(int8_t* codes_packed, const float* block_amax, int64_t M,
-                                          int64_t N, float* s_tok, hipStream_t stream) {
-  if (M < 0 || N < 64 || N % 64 != 0 || M > (int64_t)1 << 31 || N > (int64_t)1 << 30)
-    return W8A8_ERR_BAD_SHAPE;
-  if (M == 0) return W8A8_OK;
-  if (!codes_packed || !block_amax || !s_tok) return W8A8_ERR_NULL_POINTER;
-  if (!aligned16(codes_packed) || !aligned16(block_amax) || !aligned16(s_tok)) return W8A8_ERR_MISALIGNED;
-  w8a8_status st;
-  if ((st = check_device()) != W8A8_OK) return st;
-  return launched(w8a8::launch_requantize_blocks(reinterpret_cast<uint8_t*>(codes_packed), block_amax, M,
-                                                 N, s_tok, stream));
-}
-
 w8a8_status w8a8_gateup_swiglu_quant_packed(const uint16_t* x, const int8_t* w_gateup_packed,
                                             const float* s_ch, const uint16_t* bias, int64_t M,
                                             int64_t N, int64_t K, int rot_in, int rot_out,
                                             int8_t* q_packed, float* s_tok, void* workspace,
                                             size_t workspace_bytes, hipStream_t stream) {
-  w8a8_status st = check_swiglu_quant(M, N, K, rot_out);
+  w8a8_status st = check_swiglu_quant(M, N, K, rot_in, rot_out);
   if (st != W8A8_OK) return st;
-  if (rot_in != 0 && rot_in != 128) return W8A8_ERR_BAD_ARGUMENT;
   if (M == 0) return W8A8_OK;
   if (workspace_bytes < w8a8_swiglu_quant_workspace_bytes(M, N, K)) return W8A8_ERR_BAD_ARGUMENT;
   if (!x || !w_gateup_packed || !s_ch || !q_packed || !s_tok || !workspace) return W8A8_ERR_NULL_POINTER;
@@ -350,26 +309,16 @@ w8a8_status w8a8_gateup_swiglu_quant_packed(const uint16_t* x, const int8_t* w_g
       !aligned16(s_tok) || !aligned16(workspace) || (bias && !aligned16(bias)))
     return W8A8_ERR_MISALIGNED;
   if ((st = check_device()) != W8A8_OK) return st;
+  // workspace: x codes (packed) | x scales | the bf16 SwiGLU output h [M, N]
   uint8_t* qx = static_cast<uint8_t*>(workspace);
   float* s_x = reinterpret_cast<float*>(qx + align256(w8a8_packed_bytes(M, K)));
-  float* amax = reinterpret_cast<float*>(reinterpret_cast<uint8_t*>(s_x) + align256((size_t)M * sizeof(float)));
+  uint16_t* h = reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(s_x) + align256((size_t)M * sizeof(float)));
   st = launched(w8a8::launch_quantize(x, M, K, rot_in, false, /*packed=*/true, qx, s_x, stream));
   if (st != W8A8_OK) return st;
-  st = launched(w8a8::launch_gemm_swiglu_quant(qx, s_x, w_gateup_packed, s_ch, bias,
-                                               quant_out(q_packed, amax, nullptr, rot_out), M, N, K, stream));
+  st = launched(w8a8::launch_gemm(w8a8::Epi::kSwiglu, false, /*packed_a=*/true, /*packed_b=*/true, qx, s_x,
+                                  w_gateup_packed, s_ch, bias, h, M, N, K, stream));
   if (st != W8A8_OK) return st;
-  return launched(w8a8::launch_requantize_blocks(reinterpret_cast<uint8_t*>(q_packed), amax, M, N, s_tok,
-                                                 stream));
+  return launched(w8a8::launch_quantize(h, M, N, rot_out, false, /*packed=*/true, q_packed, s_tok, stream));
 }
 
 }  // extern "C"
-
-w8a8_status w8a8_mfma_probe(int kind, int64_t iters, int blocks, int32_t* sink, hipStream_t stream) {
-  if (kind != 0 && kind != 1) return W8A8_ERR_BAD_ARGUMENT;
-  if (iters < 1 || iters > ((int64_t)1 << 40) || blocks < 1 || blocks > 65536) return W8A8_ERR_BAD_SHAPE;
-  if (!sink) return W8A8_ERR_NULL_POINTER;
-  if (!aligned16(sink)) return W8A8_ERR_MISALIGNED;
-  w8a8_status st;
-  if ((st = check_device()) != W8A8_OK) return st;
-  return launched(w8a8::launch_mfma_probe(kind == 1, iters, blocks, sink, stream));
-}

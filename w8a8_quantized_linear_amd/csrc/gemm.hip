@@ -9,10 +9,7 @@
 //             card, Benefits list);
 //   kSwiglu : bf16(silu(g) * u) with g, u the dequantized values of packed rows
 //             n and N + n -- the paired gate/up epilogue ("Loading CLEF INT8",
-//             fuse_mlp; gate/up packed into one weight at load time);
-//   kSwigluQ: that SwiGLU output quantized for the next linear, first step:
-//             int8 codes of each 128-column block on the block's own scale
-//             plus the block amax (requant.hip rescales them to the row scale).
+//             fuse_mlp; gate/up packed into one weight at load time).
 // The bf16 outputs go through LDS so that stores cover whole row segments.
 //
 // Design.  Both operands are K-contiguous ("NT"), so MFMA operands load with no
@@ -46,7 +43,6 @@
 
 #include "epilogue_math.h"
 #include "internal.h"
-#include "quant_math.h"
 
 namespace w8a8 {
 namespace {
@@ -164,119 +160,6 @@ __device__ __forceinline__ void store_tile_i32(const Acc (&acc)[TN][TM], int32_t
   }
 }
 
-// kSwigluQ epilogue: the tile's 128 output columns are one block of the next
-// linear's input (its rotation block), so the tile can quantize its part of
-// every row on the block's own scale (first of the two steps that quantize the
-// SwiGLU output per token; launch_requantize_blocks is the second).
-//   1. the bf16 SwiGLU values h (as the kSwiglu epilogue computes them) go to
-//      LDS, [BM rows][128 columns], reusing the operand ring (and to qo.h when
-//      it is set); columns past N are stored as zeros;
-//   2. four lanes (a DPP quad) take a row's block, 32 values each: the exact
-//      block rotation of the quantizer (fp64 sums, one rounding to fp32) or the
-//      plain values, the block amax over the quad, s_b = amax / 127 and
-//      round-half-even codes; the codes go to the packed layout (each lane 32
-//      contiguous bytes), the amax to qo.amax[m][tile_n].
-template <int BM, int TM, int TN, int WTM, int WTN, int LDS_BYTES, typename Acc>
-__device__ __forceinline__ void swiglu_quant_tile(const Acc (&acc)[TN][TM], const float* __restrict__ s_tok,
-                                                  const float* __restrict__ s_ch,
-                                                  const uint16_t* __restrict__ bias, const QuantOut& qo,
-                                                  int64_t M, int64_t N, int64_t mb, int64_t nb, int tile_n,
-                                                  int nblk, int wm, int wn, int frag_row, int frag_half,
-                                                  uint8_t* lds, int tid) {
-  constexpr int kStride = 128 * 2 + 16;  // LDS bytes per row of h (padding spreads the banks)
-  static_assert(BM * kStride <= LDS_BYTES, "h tile fits the operand ring");
-  // scales and bias loaded first, without conditions (as in store_tile_staged)
-  const bool has_bias = bias != nullptr;
-  const uint16_t* bsrc = has_bias ? bias : reinterpret_cast<const uint16_t*>(s_ch);
-  float st[TM];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) st[tm] = s_tok[min<int64_t>(mb + wm * WTM + tm * 32 + frag_row, M - 1)];
-  float4 sg[TN / 2][4], su[TN / 2][4];
-  uint2 bg_raw[TN / 2][4], bu_raw[TN / 2][4];
-#pragma unroll
-  for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int64_t n = min<int64_t>(nb + wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half, N - 4);
-      sg[tn][q] = *reinterpret_cast<const float4*>(s_ch + n);
-      su[tn][q] = *reinterpret_cast<const float4*>(s_ch + N + n);
-      bg_raw[tn][q] = *reinterpret_cast<const uint2*>(bsrc + n);
-      bu_raw[tn][q] = *reinterpret_cast<const uint2*>(bsrc + N + n);
-    }
-  lds_barrier();  // every wave is done with the operand ring
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm) {
-    const int row_l = wm * WTM + tm * 32 + frag_row;
-    const int64_t m = mb + row_l;
-    const bool live = m < M;
-#pragma unroll
-    for (int tn = 0; tn < TN / 2; ++tn)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col_l = wn * (WTN / 2) + tn * 32 + 8 * q + 4 * frag_half;
-        const int64_t n0 = nb + col_l;
-        float bg[4], bu[4], y[4];
-        bf16x4(has_bias ? bg_raw[tn][q] : make_uint2(0u, 0u), bg);
-        bf16x4(has_bias ? bu_raw[tn][q] : make_uint2(0u, 0u), bu);
-        const float sgv[4] = {sg[tn][q].x, sg[tn][q].y, sg[tn][q].z, sg[tn][q].w};
-        const float suv[4] = {su[tn][q].x, su[tn][q].y, su[tn][q].z, su[tn][q].w};
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float g = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st[tm] * sgv[v], bg[v]);
-          const float u = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st[tm] * suv[v], bu[v]);
-          y[v] = silu_f32(g) * u;
-        }
-        uint2 hv = make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
-        if (live && n0 < N) {
-          if (qo.h) *reinterpret_cast<uint2*>(qo.h + m * N + n0) = hv;
-        } else {
-          hv = make_uint2(0u, 0u);  // columns past N enter the block amax as zeros
-        }
-        *reinterpret_cast<uint2*>(lds + row_l * kStride + col_l * 2) = hv;
-      }
-  }
-  lds_barrier();  // the tile's h is in LDS
-
-  const int lane = tid & 63, p = tid & 3;
-  const int64_t kblocks = N / 64;
-#pragma unroll 1
-  for (int pass = 0; pass < BM / 64; ++pass) {
-    const int row_l = pass * 64 + tid / 4;
-    const int64_t m = mb + row_l;
-    if (m >= M) continue;  // the whole quad: one row
-    qm::u32x4 raw[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      raw[i] = *reinterpret_cast<const qm::u32x4*>(lds + row_l * kStride + p * 64 + i * 16);
-    float y[qm::kEPL];
-    if (qo.rot) {
-      qm::rotate_chunk(raw, lane, y);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        y[2 * j] = qm::bf16lo(raw[j / 4][j % 4]);
-        y[2 * j + 1] = qm::bf16hi(raw[j / 4][j % 4]);
-      }
-    }
-    float a = 0.0f;
-#pragma unroll
-    for (int j = 0; j < qm::kEPL; ++j) a = fmaxf(a, fabsf(y[j]));
-    a = qm::group_max<4>(a);
-    const qm::QuotientScale qs = qm::quotient_scale(a / 127.0f);  // IEEE division; a zero block gives zero codes
-    qm::apply_prefactor(y, qs);
-    uint32_t w[8];
-#pragma unroll
-    for (int g = 0; g < 8; ++g) w[g] = qm::int8_codes4(y[4 * g], y[4 * g + 1], y[4 * g + 2], y[4 * g + 3], qs.s, qs.r);
-    const int64_t c0 = nb + 32 * p;  // first column of this lane's 32
-    if (c0 < N) {
-      uint8_t* dst = qo.codes + ((m / 32) * kblocks + c0 / 64) * 2048 + (m % 32) * 64 + (c0 % 64);
-      *reinterpret_cast<qm::u32x4*>(dst) = qm::u32x4{w[0], w[1], w[2], w[3]};
-      *reinterpret_cast<qm::u32x4*>(dst + 16) = qm::u32x4{w[4], w[5], w[6], w[7]};
-    }
-    if (p == 0) qo.amax[m * nblk + tile_n] = a;
-  }
-}
-
 // bf16 epilogues (kDequant, kSwiglu) staged through LDS.  In the MFMA layout a
 // lane holds 4 consecutive columns of one row, so a direct store instruction
 // writes 16 bytes into each of 32 rows -- 32 partial cache lines per
@@ -380,7 +263,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN)
 gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
           const uint8_t* __restrict__ b, const float* __restrict__ s_ch,
           const uint16_t* __restrict__ bias, void* __restrict__ out,
-          int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n, QuantOut qo) {
+          int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int CH = BK / 16;                       // 16-byte chunks per LDS row
   constexpr int NSUB = BK / 32;                     // 32-deep k substeps per stage
@@ -393,8 +276,6 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   static_assert(TM * 32 * WGM == BM && TN * 32 * WGN == BN, "wave tiles of 32x32 blocks");
   static_assert(A_LOADS * NT == BM * CH && B_LOADS * NT == BN * CH, "tile / threads");
   static_assert(!paired_epi(EPI) || TN % 2 == 0, "SwiGLU needs gate/up block pairs");
-  static_assert(EPI != Epi::kSwigluQ || (BN == 256 && BM % 64 == 0 && WGM * WGN == 4),
-                "block quantization: 128 output columns per tile, 256 threads");
   static_assert(NST * LOADS < 64, "vmcnt range");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NST * STAGE];
 
@@ -591,10 +472,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
   // the tail re-loads must land before the workgroup's LDS can be reused
   wait_vmcnt<0>();
 
-  if constexpr (EPI == Epi::kSwigluQ) {
-    swiglu_quant_tile<BM, TM, TN, WTM, WTN, NST * STAGE>(acc, s_tok, s_ch, bias, qo, M, N, mb, nb, tile_n, tiles_n, wm,
-                                            wn, frag_row, frag_half, lds, tid);
-  } else if constexpr (EPI == Epi::kRawI32) {
+  if constexpr (EPI == Epi::kRawI32) {
     store_tile_i32<TM, TN, WTM, WTN>(acc, static_cast<int32_t*>(out), M, N, mb, nb, wm, wn, frag_row, frag_half);
   } else {
     constexpr int REGION = WTM * (EPI == Epi::kSwiglu ? WTN / 2 : WTN) * 2;
@@ -607,7 +485,7 @@ gemm_tile(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
 template <int BM, int BN, int WGM, int WGN, int BK, int NST, Epi EPI, bool FP8, bool PA, bool PB>
 hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const float* s_ch,
                       const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
-                      hipStream_t stream, const QuantOut& qo = QuantOut{}) {
+                      hipStream_t stream) {
   const int64_t tiles_m = (M + BM - 1) / BM;
   const int64_t cols_per_tile = paired_epi(EPI) ? BN / 2 : BN;
   const int64_t tiles_n = (N + cols_per_tile - 1) / cols_per_tile;
@@ -617,7 +495,7 @@ hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const fl
   hipLaunchKernelGGL((gemm_tile<BM, BN, WGM, WGN, BK, NST, EPI, FP8, PA, PB>), dim3((unsigned)blocks),
                      dim3(64 * WGM * WGN), 0, stream, static_cast<const uint8_t*>(a), s_tok,
                      static_cast<const uint8_t*>(b), s_ch, bias, out, M, N, K, (int)tiles_m,
-                     (int)tiles_n, qo);
+                     (int)tiles_n);
   return hipGetLastError();
 }
 
@@ -687,26 +565,13 @@ hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const vo
   }
   switch (epi) {
     case Epi::kRawI32:
-      if (packed_a || packed_b) return hipErrorInvalidValue;
-      return launch_t<Epi::kRawI32, false, false, false>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+      return launch_layouts<Epi::kRawI32, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
     case Epi::kDequant:
       return launch_layouts<Epi::kDequant, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
     case Epi::kSwiglu:
       return launch_layouts<Epi::kSwiglu, false>(packed_a, packed_b, a, s_tok, b, s_ch, bias, out, M, N, K, stream);
-    case Epi::kSwigluQ:  // launch_gemm_swiglu_quant
-      return hipErrorInvalidValue;
   }
   return hipErrorInvalidValue;
-}
-
-// The 256 x 256 tile: 128 output columns per tile, one block of the next
-// linear's input.
-hipError_t launch_gemm_swiglu_quant(const void* a, const float* s_tok, const void* b,
-                                    const float* s_ch, const uint16_t* bias, const QuantOut& qo,
-                                    int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (N % 64 != 0 || (qo.rot != 0 && (qo.rot != 128 || N % 128 != 0))) return hipErrorInvalidValue;
-  return launch_cfg<256, 256, 2, 2, 64, 4, Epi::kSwigluQ, false, true, true>(a, s_tok, b, s_ch, bias, nullptr,
-                                                                          M, N, K, stream, qo);
 }
 
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream) {

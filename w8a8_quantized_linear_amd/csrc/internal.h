@@ -7,20 +7,11 @@
 
 namespace w8a8 {
 
-// Epilogues of the GEMM kernel.  kSwigluQ: the SwiGLU output quantized for the
-// next linear, first step (block codes + block amax, see launch_gemm_swiglu_quant).
-enum class Epi : int { kRawI32 = 0, kDequant = 1, kSwiglu = 2, kSwigluQ = 3 };
+// Epilogues of the GEMM kernel.
+enum class Epi : int { kRawI32 = 0, kDequant = 1, kSwiglu = 2 };
 
 // Epilogues that pair gate rows n with up rows N + n.
-constexpr bool paired_epi(Epi e) { return e == Epi::kSwiglu || e == Epi::kSwigluQ; }
-
-// Outputs of the kSwigluQ epilogue.
-struct QuantOut {
-  uint8_t* codes = nullptr;  // block codes, packed [M, N] (N % 64 == 0)
-  float* amax = nullptr;     // [M, nblk], nblk = ceil(N / 128)
-  uint16_t* h = nullptr;     // optional bf16 SwiGLU output [M, N] (nullptr: not written)
-  int rot = 0;               // 128: blocks are rotated before quantization (N % 128 == 0)
-};
+constexpr bool paired_epi(Epi e) { return e == Epi::kSwiglu; }
 
 // Packed operand layout: blocks of 32 rows x 64 bytes, block (r / 32, k / 64) at
 // byte ((r / 32) * (K / 64) + k / 64) * 2048, row r % 32 of the block at + 64 * (r % 32).
@@ -36,17 +27,6 @@ hipError_t launch_quantize(const uint16_t* x, int64_t M, int64_t K, int rot_bloc
 hipError_t launch_gemm(Epi epi, bool fp8, bool packed_a, bool packed_b, const void* a,
                        const float* s_tok, const void* b, const float* s_ch, const uint16_t* bias,
                        void* out, int64_t M, int64_t N, int64_t K, hipStream_t stream);
-
-// Gate/up GEMM whose epilogue quantizes the SwiGLU output per 128-column block:
-// a and b packed (a [M, K], b [2N, K]); writes qo.codes, qo.amax (and qo.h).
-hipError_t launch_gemm_swiglu_quant(const void* a, const float* s_tok, const void* b,
-                                    const float* s_ch, const uint16_t* bias, const QuantOut& qo,
-                                    int64_t M, int64_t N, int64_t K, hipStream_t stream);
-
-// Second step: block codes (packed [M, N], rewritten in place) rescaled to the
-// row scale s [M] = max_b amax[m][b] / 127.
-hipError_t launch_requantize_blocks(uint8_t* codes, const float* amax, int64_t M, int64_t N,
-                                    float* s, hipStream_t stream);
 
 // y [M, N] (dense) = bf16(silu(g) * u), g and u bf16 [M, N] with rows ld elements
 // apart (N % 8 == 0, ld % 8 == 0).
@@ -67,10 +47,5 @@ hipError_t launch_linear_short(Epi epi, const uint16_t* x, const void* w, bool w
 
 // Row-major codes [rows, K] -> packed layout (K % 64 == 0; padding rows zero).
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream);
-
-// Measurement aid (not on the path): `blocks` workgroups of 4 waves, each wave
-// `iters` rounds of four independent MFMAs with register operands (int8
-// 32x32x32, or bf16 32x32x16 when bf16); sink [blocks * 256] int32.
-hipError_t launch_mfma_probe(bool bf16, int64_t iters, int blocks, int32_t* sink, hipStream_t stream);
 
 }  // namespace w8a8
