@@ -71,7 +71,9 @@ typedef enum {
   W8A8_ERR_MISALIGNED = 3,         /* a pointer is not 16-byte aligned */
   W8A8_ERR_BAD_ARGUMENT = 4,       /* rot_block not 0/128, or the workspace is too small */
   W8A8_ERR_UNSUPPORTED_DEVICE = 5, /* no HIP device, or the current device is not gfx950 */
-  W8A8_ERR_LAUNCH = 6              /* the kernel launch itself failed (hipGetLastError) */
+  W8A8_ERR_LAUNCH = 6,             /* the kernel launch itself failed (hipGetLastError) */
+  W8A8_ERR_SCRATCH_TOO_SMALL = 7   /* w8a8_linear_packed_noalloc: the call needs more than
+                                      W8A8_NOALLOC_MAX_WORKSPACE bytes of scratch */
 } w8a8_status;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -231,6 +233,26 @@ w8a8_status w8a8_fp8_linear_packed(const uint16_t* x, const uint8_t* w_packed, c
                                    const uint16_t* bias, uint16_t* y, int64_t M, int64_t N, int64_t K,
                                    int rot_block, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream);
+
+/* ---- the int8 whole path without a workspace ---------------------------------
+ * For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): w8a8_linear_packed with
+ * its workspace -- the packed activation codes and their scales -- taken from a
+ * fixed device array inside the library instead of the caller.  Same kernels,
+ * same arguments otherwise, same results byte for byte.  The array holds
+ * W8A8_NOALLOC_MAX_WORKSPACE bytes on each device the library runs on, kept until
+ * the process ends; a call whose w8a8_workspace_bytes(M, K) exceeds it returns
+ * W8A8_ERR_SCRATCH_TOO_SMALL (checked after the shapes, before anything else)
+ * and enqueues nothing.  This entry point allocates nothing (no hipMalloc, no
+ * library allocation).  Every call on one device shares that device's array:
+ * calls that overlap in time on one device (e.g. on two streams) race and give
+ * undefined results; calls ordered on one stream are safe.  The array keeps the
+ * last call's codes and scales; nothing in it needs clearing between calls. */
+#define W8A8_NOALLOC_MAX_WORKSPACE (64u << 20)
+
+w8a8_status w8a8_linear_packed_noalloc(const uint16_t* x, const int8_t* w_packed, const float* s_ch,
+                                       const uint16_t* bias, uint16_t* y, int64_t M, int64_t N,
+                                       int64_t K, int rot_block, hipStream_t stream);
 
 /* ---- gate/up SwiGLU whose output is quantized for the next linear -----------
  * The down projection that follows the gate/up pair is an INT8 projection too,

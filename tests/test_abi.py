@@ -15,7 +15,7 @@ ROOT = Path(__file__).resolve().parents[1]
 HEADER = ROOT / "include" / "w8a8.h"
 LIB = ROOT / "w8a8_quantized_linear_amd" / "libw8a8.so"
 
-OK, NULLP, SHAPE, MISALIGNED, BADARG, DEVICE = 0, 1, 2, 3, 4, 5
+OK, NULLP, SHAPE, MISALIGNED, BADARG, DEVICE, LAUNCH, SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 A = 0x10000   # a 16-byte aligned dummy address (never dereferenced)
 U = A + 8     # misaligned
 
@@ -53,6 +53,7 @@ def lib():
         "w8a8_fp8_linear_packed": (I, [P, P, P, P, P, I64, I64, I64, I, P, SZ, P]),
         "w8a8_swiglu_quant_workspace_bytes": (SZ, [I64, I64, I64]),
         "w8a8_gateup_swiglu_quant_packed": (I, [P, P, P, P, I64, I64, I64, I, I, P, P, P, SZ, P]),
+        "w8a8_linear_packed_noalloc": (I, [P, P, P, P, P, I64, I64, I64, I, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -94,7 +95,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for s in range(7):
+    for s in range(8):
         assert lib.w8a8_status_string(s).decode().startswith("W8A8_")
     assert b"unknown" in lib.w8a8_status_string(99)
 
@@ -224,6 +225,29 @@ def test_swiglu_quant_sizes_and_argument_checks(lib):
     assert g(A, A, A, None, 4, 256, 320, 0, 0, A, A, A, ws, None) == SHAPE      # K % 128
     assert g(A, A, A, None, 4, 131072 + 128, 512, 0, 0, A, A, A, 1 << 40, None) == SHAPE  # N too long
     assert g(None, None, None, None, 0, 256, 512, 0, 0, None, None, None, 0, None) == OK
+
+
+def test_noalloc_argument_checks(lib):
+    """The entry point without a workspace: the allocating entry point's checks, and the
+    fixed scratch limit (64 MiB) right after the shapes."""
+    f = lib.w8a8_linear_packed_noalloc
+    assert b"scratch" in lib.w8a8_status_string(SCRATCH)
+    assert f(A, A, A, None, A, 4, 8, 192, 0, None) == SHAPE                    # K % 128
+    assert f(A, A, A, None, A, 4, 8, 256, 3, None) == BADARG                   # rot_block
+    assert f(None, None, None, None, None, 0, 8, 256, 0, None) == OK           # M == 0
+    assert f(A, A, A, None, None, 4, 8, 256, 0, None) == NULLP
+    assert f(A, A, U, None, A, 4, 8, 256, 0, None) == MISALIGNED
+    assert f(A, A, A, U, A, 4, 8, 256, 0, None) == MISALIGNED                  # bias
+    # 12,016 x 17,408: 209 MB of codes, beyond the 64 MiB array (before any pointer check)
+    assert f(None, None, None, None, None, 12016, 5120, 17408, 128, None) == SCRATCH
+    # the boundary: 4,096 x 16,384 codes are 64 MiB, plus 16 KiB of scales -> too large;
+    # 4,064 rows fit
+    assert lib.w8a8_workspace_bytes(4096, 16384) == (64 << 20) + 16384
+    assert f(A, A, A, None, A, 4096, 8, 16384, 0, None) == SCRATCH
+    assert lib.w8a8_workspace_bytes(4064, 16384) <= 64 << 20
+    import torch
+    if not torch.cuda.is_available():
+        assert f(A, A, A, None, A, 4064, 8, 16384, 0, None) == DEVICE
 
 
 def test_packed_i32_argument_checks(lib):

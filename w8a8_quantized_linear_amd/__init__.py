@@ -29,7 +29,7 @@ __all__ = [
     "w8a8_fp8_linear_packed", "w8a8_quantize_act_packed", "w8a8_quantize_act_fp8_packed",
     "w8a8_gemm_dequant_packed", "w8a8_gemm_swiglu_packed", "w8a8_fp8_gemm_dequant_packed",
     "w8a8_swiglu", "swiglu_quant_workspace_bytes", "w8a8_gateup_swiglu_quant_packed",
-    "w8a8_gemm_i32_packed", "swiglu_quant_h",
+    "w8a8_gemm_i32_packed", "swiglu_quant_h", "w8a8_linear_packed_noalloc", "NOALLOC_MAX_WORKSPACE",
 ]
 
 LIB_PATH = Path(__file__).resolve().parent / "libw8a8.so"
@@ -65,6 +65,7 @@ _SIGS = {
     "w8a8_gateup_swiglu_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_fp8_linear_packed": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P, _SZ, _P]),
     "w8a8_swiglu_quant_workspace_bytes": (_SZ, [_I64, _I64, _I64]),
+    "w8a8_linear_packed_noalloc": (_I, [_P, _P, _P, _P, _P, _I64, _I64, _I64, _I, _P]),
     "w8a8_gateup_swiglu_quant_packed": (_I, [_P, _P, _P, _P, _I64, _I64, _I64, _I, _I, _P, _P, _P, _SZ, _P]),
 }
 for _name, (_res, _args) in _SIGS.items():
@@ -405,6 +406,31 @@ def w8a8_fp8_linear_packed(x, w_packed, N, s_ch, bias=None, rot_block=0, workspa
     """w8a8_fp8_linear with the E4M3FN weight [N, K] given in the packed layout."""
     return _path("w8a8_fp8_linear_packed", x, w_packed, s_ch, bias, rot_block, N, torch.uint8,
                  workspace, out, w_rows=N)
+
+
+# Bytes of the library's fixed scratch array (W8A8_NOALLOC_MAX_WORKSPACE in w8a8.h).
+NOALLOC_MAX_WORKSPACE = 64 << 20
+
+
+def w8a8_linear_packed_noalloc(x, w_packed, N, s_ch, bias=None, rot_block=0, out=None):
+    """w8a8_linear_packed with no workspace: the C entry point keeps the quantized
+    activations in the library's fixed per-device scratch array and allocates nothing
+    (y is allocated here only when `out` is not given).  Calls that overlap in time on
+    one device race; workspace_bytes(M, K) must not exceed NOALLOC_MAX_WORKSPACE."""
+    _want(x, torch.bfloat16, "x", 2)
+    _want(w_packed, torch.int8, "w_packed", 1)
+    _want(s_ch, torch.float32, "s_ch", 1)
+    if bias is not None:
+        _want(bias, torch.bfloat16, "bias", 1)
+    M, K = x.shape
+    if w_packed.numel() < packed_bytes(N, K):
+        raise ValueError("packed weight is smaller than packed_bytes(N, K)")
+    if s_ch.shape[0] != N or (bias is not None and bias.shape[0] != N):
+        raise ValueError("s_ch and bias lengths must equal N")
+    y = _out(out, torch.bfloat16, M * N, "out", x.device, shape=(M, N))
+    _check(_lib.w8a8_linear_packed_noalloc(_ptr(x), _ptr(w_packed), _ptr(s_ch), _ptr(bias), _ptr(y), M, N, K,
+                                           rot_block, _stream()), "w8a8_linear_packed_noalloc")
+    return y
 
 
 # ------------------------ gate/up SwiGLU quantized for the next linear -------

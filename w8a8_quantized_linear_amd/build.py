@@ -24,7 +24,7 @@ BUILD_DIR = PKG / "_build"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "scratch.hip", "api.cpp"]
 # measurement aids for the benchmark and the design tests (not the library's C ABI)
 PROBE_DIR = PKG / "probe"
 PROBE_SOURCES = ["mfma_probe.hip", "fp8_contraction.hip"]

@@ -79,6 +79,32 @@ w8a8_status gemm_epilogue(w8a8::Epi epi, bool fp8, bool packed, const void* q, c
   return launched(w8a8::launch_gemm(epi, fp8, packed, packed, q, s_tok, w, s_ch, bias, y, M, N, K, stream));
 }
 
+}  // namespace
+
+namespace w8a8 {
+
+w8a8_status whole_path_shape_checks(int64_t M, int64_t N, int64_t K, int rot_block) {
+  w8a8_status st = check_gemm_shape(M, N, K);
+  if (st != W8A8_OK) return st;
+  if (rot_block != 0 && rot_block != 128) return W8A8_ERR_BAD_ARGUMENT;
+  return W8A8_OK;
+}
+
+w8a8_status whole_path_checks(const void* x, const void* w, const float* s_ch, const uint16_t* bias,
+                              const void* y, int64_t M, int64_t N, int64_t K, int rot_block) {
+  w8a8_status st = whole_path_shape_checks(M, N, K, rot_block);
+  if (st != W8A8_OK) return st;
+  if (M == 0) return W8A8_OK;
+  if (!x || !w || !s_ch || !y) return W8A8_ERR_NULL_POINTER;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(s_ch) || !aligned16(y) || (bias && !aligned16(bias)))
+    return W8A8_ERR_MISALIGNED;
+  return W8A8_OK;
+}
+
+}  // namespace w8a8
+
+namespace {
+
 // Whole path: quantize x into the workspace (packed layout), then the GEMM +
 // epilogue against a row-major or packed weight.
 w8a8_status whole_path(w8a8::Epi epi, bool fp8, bool w_packed, const uint16_t* x, const void* w,
@@ -90,10 +116,9 @@ w8a8_status whole_path(w8a8::Epi epi, bool fp8, bool w_packed, const uint16_t* x
   if (rot_block != 0 && rot_block != 128) return W8A8_ERR_BAD_ARGUMENT;
   if (M == 0) return W8A8_OK;
   if (workspace_bytes < w8a8_workspace_bytes(M, K)) return W8A8_ERR_BAD_ARGUMENT;
-  if (!x || !w || !s_ch || !y || !workspace) return W8A8_ERR_NULL_POINTER;
-  if (!aligned16(x) || !aligned16(w) || !aligned16(s_ch) || !aligned16(y) || !aligned16(workspace) ||
-      (bias && !aligned16(bias)))
-    return W8A8_ERR_MISALIGNED;
+  if (!workspace) return W8A8_ERR_NULL_POINTER;
+  if (!aligned16(workspace)) return W8A8_ERR_MISALIGNED;
+  if ((st = w8a8::whole_path_checks(x, w, s_ch, bias, y, M, N, K, rot_block)) != W8A8_OK) return st;
   if ((st = check_device()) != W8A8_OK) return st;
   uint8_t* q = static_cast<uint8_t*>(workspace);
   float* s_tok = reinterpret_cast<float*>(q + align256(w8a8_packed_bytes(M, K)));
@@ -132,6 +157,9 @@ const char* w8a8_status_string(w8a8_status s) {
     case W8A8_ERR_BAD_ARGUMENT: return "W8A8_ERR_BAD_ARGUMENT: rot_block not 0/128 or workspace too small";
     case W8A8_ERR_UNSUPPORTED_DEVICE: return "W8A8_ERR_UNSUPPORTED_DEVICE: no gfx950 HIP device is current";
     case W8A8_ERR_LAUNCH: return "W8A8_ERR_LAUNCH: kernel launch failed";
+    case W8A8_ERR_SCRATCH_TOO_SMALL:
+      return "W8A8_ERR_SCRATCH_TOO_SMALL: the call needs more than the library's fixed scratch buffer "
+             "(W8A8_NOALLOC_MAX_WORKSPACE bytes); use the entry point that takes a workspace";
   }
   return "W8A8 unknown status";
 }

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <cstdint>
 
+#include "w8a8.h"
+
 namespace w8a8 {
 
 // Epilogues of the GEMM kernel.
@@ -44,6 +46,14 @@ hipError_t launch_linear_short(Epi epi, const uint16_t* x, const void* w, bool w
                                const float* s_ch, const uint16_t* bias, uint16_t* y, int64_t M,
                                int64_t N, int64_t K, int rot_block, void* q_ws, float* s_ws,
                                hipStream_t stream);
+
+// Argument checks of the whole-path entry points except the workspace and the
+// device, in the library's order: shapes, rot_block, (M == 0: OK), pointers,
+// alignment.
+w8a8_status whole_path_checks(const void* x, const void* w, const float* s_ch, const uint16_t* bias,
+                              const void* y, int64_t M, int64_t N, int64_t K, int rot_block);
+// The shape and rot_block part of those checks alone.
+w8a8_status whole_path_shape_checks(int64_t M, int64_t N, int64_t K, int rot_block);
 
 // Row-major codes [rows, K] -> packed layout (K % 64 == 0; padding rows zero).
 hipError_t launch_pack_rows(const void* src, int64_t rows, int64_t K, void* dst, hipStream_t stream);
