@@ -25,6 +25,11 @@ BUILD_DIR = PKG / "_build"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "scratch.hip", "api.cpp"]
+# Per-source flags.  The quantizer's fp64 matrix instructions (the rotation's
+# cross-quarter transform) take the VGPR form: their results feed vector
+# instructions, and results in accumulation registers would cost two copies per
+# value and, at 12,016 x 17,408, the third wave per SIMD.
+EXTRA = {"quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # measurement aids for the benchmark and the design tests (not the library's C ABI)
 PROBE_DIR = PKG / "probe"
 PROBE_SOURCES = ["mfma_probe.hip", "fp8_contraction.hip"]
@@ -43,7 +48,7 @@ def _compile(src: str, folder: Path = CSRC, tag: str = "") -> Path:
     obj = BUILD_DIR / (tag + src.rsplit(".", 1)[0] + ".o")
     obj.unlink(missing_ok=True)
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", str(folder / src), "-o", str(obj)]
+    cmd = [HIPCC, *COMMON, *EXTRA.get(src, []), *lang, "-c", str(folder / src), "-o", str(obj)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature for this target (ignoring feature)"
     err = "\n".join(l for l in res.stderr.splitlines() if noise not in l)

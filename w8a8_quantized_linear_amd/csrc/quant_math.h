@@ -1,6 +1,5 @@
 // Device-side arithmetic of the per-row quantizer, shared by the quantizer
-// kernel, the single-launch short-input path and the GEMM epilogue that
-// quantizes the SwiGLU output (no state; header-only).
+// kernel and the single-launch short-input path (no state; header-only).
 //
 // The rotation, scale and code rules follow the per-token activation quantizer
 // of the ConvRot INT8 path ("CLEF Calibrated INT8 ConvRot" card, notes under the
@@ -123,13 +122,17 @@ __device__ __forceinline__ uint32_t int8_codes4(float y0, float y1, float y2, fl
   return lo | hi;
 }
 
-// Exact rotation of one 32-element chunk: the lane holds elements 32p .. 32p+31
-// of a 128-block, p = lane % 4 (its position in a DPP quad whose other lanes
-// hold the rest of the block).  Block sums of the bf16 values are formed in
-// fp64 -- 5 butterfly stages inside the lane, the last 2 across the quad --
-// then multiplied by fl64(2^-3.5) and rounded once to fp32.
-__device__ __forceinline__ void rotate_chunk(const u32x4 (&raw)[4], int lane, float (&y)[kEPL]) {
-  double v[kEPL];
+// The 128-point transform factors over the element index e = 32p + t: with
+// j = 32q + u, H128[j][e] = H4[q][p] * H32[u][t] (Sylvester sign (-1)^popcount(j & e)).
+// A lane holds the 32 elements of one quarter p of a block: it forms the 32-point
+// transform of its quarter in fp64 (5 butterfly stages), and the 4-point transform
+// across the block's 4 quarters combines lanes.  The block sums of the bf16 values
+// are exact in fp64 (8-bit significands; unless the block's exponent spread
+// exceeds ~38 bits), in any order; they are multiplied by fl64(2^-3.5) and rounded
+// once to fp32.
+
+// bf16 pairs -> fp64, then the in-lane 32-point transform.
+__device__ __forceinline__ void transform32(const u32x4 (&raw)[4], double (&v)[kEPL]) {
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const uint32_t w = raw[j / 4][j % 4];
@@ -148,6 +151,20 @@ __device__ __forceinline__ void rotate_chunk(const u32x4 (&raw)[4], int lane, fl
       }
     }
   }
+}
+
+// fl32(fl64(v * 2^-3.5)) for the lane's 32 transformed values.
+__device__ __forceinline__ void scale_to_f32(const double (&v)[kEPL], float (&y)[kEPL]) {
+#pragma unroll
+  for (int j = 0; j < kEPL; ++j) y[j] = (float)(v[j] * kInvSqrt128);
+}
+
+// Exact rotation of one 32-element chunk, quarters in DPP quads: the lane holds
+// quarter p = lane % 4 of its block (the other lanes of its quad hold the rest);
+// the 4-point transform takes two exchange stages of quad_perm moves.
+__device__ __forceinline__ void rotate_chunk(const u32x4 (&raw)[4], int lane, float (&y)[kEPL]) {
+  double v[kEPL];
+  transform32(raw, v);
   // element index bits 5, 6 are the lane's position in its quad
   // (lower lane: v + p; upper lane: p - v; both exact)
   {
@@ -160,8 +177,29 @@ __device__ __forceinline__ void rotate_chunk(const u32x4 (&raw)[4], int lane, fl
 #pragma unroll
     for (int j = 0; j < kEPL; ++j) v[j] = __builtin_fma(sgn, v[j], quad_xor<2>(v[j]));
   }
+  scale_to_f32(v, y);
+}
+
+// Exact rotation of one 32-element chunk, quarters 16 lanes apart: lane
+// 16p + n holds quarter p of the block of column n (n < 16), so a wave holds 16
+// blocks.  The 4-point transform across quarters is a matrix product on the fp64
+// matrix core: v_mfma_f64_4x4x4f64 runs 4 independent 4x4x4 products, one per
+// lane group of equal bits 2-3, with B[k][j] = lane 16k + 4b + j, A[i][k] = lane
+// 16k + 4b + i and D[i][j] = lane 16i + 4b + j (b = the group; layout checked by
+// a GPU probe).  B is a value of quarter k of column 4b + j, A = H4, so D at
+// lane 16q + n is sum_k H4[q][k] * (quarter k of column n): quarter q of the
+// transform, landing in the lane that holds quarter q.  Products with +-1 are
+// exact and the sums are those of the exact block sums, so the result is the
+// quad form's bit for bit; the matrix core takes the 64 cross-lane products
+// per value off the vector ALU, which the exact rotation keeps busy.
+__device__ __forceinline__ void rotate_chunk_x16(const u32x4 (&raw)[4], int lane, float (&y)[kEPL]) {
+  double v[kEPL];
+  transform32(raw, v);
+  // A[i][k] at lane 16k + 4b + i: H4[i][k] = (-1)^popcount(i & k)
+  const double h = (__builtin_popcount((lane >> 4) & lane & 3) & 1) ? -1.0 : 1.0;
 #pragma unroll
-  for (int j = 0; j < kEPL; ++j) y[j] = (float)(v[j] * kInvSqrt128);
+  for (int j = 0; j < kEPL; ++j) v[j] = __builtin_amdgcn_mfma_f64_4x4x4f64(h, v[j], 0.0, 0, 0, 0);
+  scale_to_f32(v, y);
 }
 
 }  // namespace qm

@@ -17,10 +17,13 @@
 //     load instruction reads one contiguous kilobyte.
 //   * Rotation is exact: the block sums of 128 bf16 values are formed in fp64
 //     (exact for 8-bit significands unless the block's exponent spread exceeds
-//     ~38 bits) -- 5 butterfly stages inside a lane, the last 2 across the 4
-//     lanes of a DPP quad (quad_perm moves, no LDS) -- then multiplied by
-//     fl64(2^-3.5) and rounded once to fp32.  The codes are therefore those of
-//     the exactly rotated row.
+//     ~38 bits) -- the 32-point transform of each quarter block inside its lane
+//     (5 butterfly stages), the 4-point transform across the quarters, which sit
+//     16 lanes apart, on the fp64 matrix core (one v_mfma_f64_4x4x4f64 per
+//     value, instead of two stages of cross-lane moves and FMAs on the vector
+//     ALU, which the rotation keeps busy) -- then multiplied by fl64(2^-3.5) and
+//     rounded once to fp32.  The codes are therefore those of the exactly
+//     rotated row.
 //   * amax by wave butterfly plus an LDS step across the row's waves.
 //   * Codes from the exact quotient fl32(y / s), formed from r = fl32(1/s)
 //     with one multiply and two FMAs (a correctly rounded reciprocal makes one
@@ -73,18 +76,21 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
   typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
   typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
   // A lane's chunk i is four pieces of 8 elements.  With rotation the pieces are
-  // consecutive (32 contiguous elements: a quarter of a 128-block per lane).
+  // consecutive (32 contiguous elements: a quarter of a 128-block per lane; lane
+  // 16p + n holds quarter p of column n, so a wave's chunk covers 16 consecutive
+  // blocks, 4 KB, each load instruction touching the same 64 16-byte pieces of
+  // them as any other lane order would).
   // Without rotation any placement works, so the wave's 64 lanes take
   // consecutive 16-byte pieces of a 2048-element span: every load and store
   // instruction then covers one contiguous kilobyte (half as many cache lines
   // per instruction as 64-byte-strided lanes).
   auto piece = [&](int i, int p) -> int {
-    if constexpr (ROT) return (i * T + tid) * kEPL + 8 * p;
+    if constexpr (ROT) return ((i * (T / 64) + tid / 64) * 16 + (lane & 15)) * 128 + (lane >> 4) * kEPL + 8 * p;
     else return (i * (T / 64) + tid / 64) * (64 * kEPL) + p * 512 + lane * 8;
   };
   // Every load is unconditional, and all are issued before any arithmetic: a piece
-  // past K re-reads a piece of the row's first block (with rotation the lane's quad
-  // reads the whole first block, so its rotated values are that block's), which leaves
+  // past K re-reads a piece of the row's first block (with rotation the 4 lanes of
+  // the column read the whole first block, so their rotated values are that block's), which leaves
   // the amax unchanged and is never stored.  (Conditional loads let the compiler wait
   // for the first pieces before issuing the rest: 191 against 170 us at
   // 12,016 x 17,408 rotated.  Plain loads rather than non-temporal ones: 170 -> 160 us.)
@@ -94,7 +100,7 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int e = piece(i, v);
-      const int src = e < K ? e : (ROT ? (tid & 3) * kEPL + 8 * v : 8 * v);
+      const int src = e < K ? e : (ROT ? (lane >> 4) * kEPL + 8 * v : 8 * v);
       raw[i][v] = *reinterpret_cast<const u32x4*>(xr + src);
     }
   __builtin_amdgcn_sched_barrier(0);
@@ -104,7 +110,7 @@ quantize_rows(const uint16_t* __restrict__ x, int64_t M, int K, uint8_t* __restr
 #pragma unroll
   for (int i = 0; i < CMAX; ++i) {
     if constexpr (ROT) {
-      rotate_chunk(raw[i], lane, y[i]);
+      rotate_chunk_x16(raw[i], lane, y[i]);
     } else {
 #pragma unroll
       for (int j = 0; j < 16; ++j) {
