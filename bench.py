@@ -92,6 +92,13 @@ def parse():
                     help="instead of the workload: the rate the matrix cores sustain with register "
                          "operands and no memory traffic (int8 32x32x32 and bf16 32x32x16 MFMAs), "
                          "after a ramp-up launch -- the measured-clock ceiling for the GEMM")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="instead of the workload line: the vendor library's GEMM on each large workload's "
+                         "shape (hipBLASLt through torch: torch._int_mm, int8 -> int32, for the int8 "
+                         "workloads; torch._scaled_mm with row-wise scales, E4M3FN -> bf16, for fp8) "
+                         "beside this library's GEMM on the same codes (w8a8_gemm_i32_packed, or the "
+                         "fp8 dequant GEMM), event-timed after a clock ramp -- context for the GEMM's "
+                         "roofline fraction")
     ap.add_argument("--drift", action="store_true",
                     help="instead of timing: relative L2 drift of every workload's W8A8 output from "
                          "the fp64 unquantized projection, without and with the block rotation")
@@ -237,6 +244,62 @@ def mfma_peak(torch, blocks=768, launch_s=0.2):
     return out
 
 
+def vendor_gemm(torch, W, lib, names, launches=20):
+    """Per-launch time of the vendor GEMM and of this library's GEMM on the same codes."""
+    dev = torch.device("cuda:0")
+
+    def per_launch_us(fn):
+        t = time.perf_counter()
+        while time.perf_counter() - t < RAMP_SECONDS:   # clock ramp, untimed
+            fn()
+            torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(launches):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / launches * 1e3
+
+    for name in names:
+        wl = W.WORKLOADS[name]
+        inp = W.make_inputs(wl)
+        M, K, Nw = wl.M, wl.K, wl.n_w
+        fp8 = wl.kind == "fp8"
+        quant = lib.w8a8_quantize_act_fp8 if fp8 else lib.w8a8_quantize_act
+        q, s_tok = quant(inp.x.to(dev), wl.rot_block)
+        w, s_ch = quant(inp.w.to(dev), wl.rot_block)
+        qp, wp = lib.w8a8_pack_weight(q), lib.w8a8_pack_weight(w)
+        ops = 2 * M * Nw * K
+        rec = {"vendor_gemm": name, "M": M, "K": K, "weight_rows": Nw, "ops": ops}
+        if fp8:
+            a8, b8 = q.view(torch.float8_e4m3fn), w.view(torch.float8_e4m3fn)
+            sa, sb = s_tok.view(M, 1).contiguous(), s_ch.view(1, Nw).contiguous()
+            out = torch.empty((M, Nw), dtype=torch.bfloat16, device=dev)
+            vendor = ("torch._scaled_mm (hipBLASLt), E4M3FN x E4M3FN, row-wise scales -> bf16",
+                      lambda: torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16))
+            ours = [("library", ("w8a8_fp8_gemm_dequant_packed (bf16 output)",
+                                 lambda: lib.w8a8_fp8_gemm_dequant_packed(qp, s_tok, wp, s_ch, K, out=out)))]
+        else:
+            acc = torch.empty((M, Nw), dtype=torch.int32, device=dev)
+            out = torch.empty((M, wl.N), dtype=torch.bfloat16, device=dev)
+            gemm = lib.w8a8_gemm_swiglu_packed if wl.kind == "gateup" else lib.w8a8_gemm_dequant_packed
+            vendor = ("torch._int_mm (hipBLASLt), int8 x int8 -> int32", lambda: torch._int_mm(q, w.t()))
+            ours = [("library_i32", ("w8a8_gemm_i32_packed (int32 output, as the vendor call)",
+                                     lambda: lib.w8a8_gemm_i32_packed(qp, wp, M, Nw, K, out=acc))),
+                    ("library", (f"{gemm.__name__} (the path's GEMM: fused epilogue, bf16 output)",
+                                 lambda: gemm(qp, s_tok, wp, s_ch, K, out=out)))]
+        for key, (what, fn) in [("vendor", vendor)] + ours:
+            try:
+                us = per_launch_us(fn)
+                rec[key] = {"call": what, "us_per_launch": us, "tops": ops / us / 1e6}
+            except Exception as e:   # a library without the kernel on this build: say so
+                rec[key] = {"call": what, "error": repr(e)[:200]}
+        print(json.dumps(rec), flush=True)
+        del q, w, qp, wp
+        torch.cuda.empty_cache()
+
+
 def main():
     args = parse()
     if args.pmc_summary:
@@ -257,6 +320,9 @@ def main():
 
     if args.mfma_peak:
         print(json.dumps({"mfma_peak": mfma_peak(torch)}))
+        return
+    if args.vendor_gemm:
+        vendor_gemm(torch, W, lib, [n for n in W.ORDER if W.WORKLOADS[n].M >= 2048])
         return
     if args.drift:
         import numpy as np
@@ -428,7 +494,9 @@ def main():
     out_bytes = M * out_cols * 2                             # bf16 output
     g_bytes = M * K + Nw * K + 4 * (M + Nw) + out_bytes + (0 if bias0 is None else 2 * Nw)
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
-    traffic = stored_traffic(wl.name + ("-unfused" if unfused else "") + ("-swiglu-quant" if quantout else ""))
+    # (a stored record covers the GEMM kernel alone, not the single whole-path call)
+    traffic = None if single else stored_traffic(wl.name + ("-unfused" if unfused else "")
+                                                 + ("-swiglu-quant" if quantout else ""))
 
     out = {
         "metric": "W8A8 linear TOPS incl. quant+dequant, % int8 MFMA peak; quantizer GB/s",

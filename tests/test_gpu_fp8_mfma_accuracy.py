@@ -17,6 +17,11 @@ fp8 MFMA route's error and tolerance outcome is measured and printed, and the
 library's choice (bf16 route) is asserted to be the one that passes -- if a route
 through the fp8 instructions met the tolerance, this test fails, flagging that the
 GEMM should move onto it.
+
+A second, independent fp8-MFMA implementation is measured the same way: the vendor
+library's fp8 GEMM (hipBLASLt through torch._scaled_mm, row-wise scales, bf16 output)
+on the fp8 workload at its full size (16,384 x 4,096 x 12,288), with codes and scales
+from the oracle's quantizer, on sampled rows against the oracle's epilogue.
 """
 import numpy as np
 import pytest
@@ -74,3 +79,31 @@ def test_fp8_contraction_accuracy(probe, orc):
     # the fp8 instructions: measured; none meets the output tolerance at this shape
     for kind in ("fp8_32x32x16", "f8f6f4_32x32x64", "fp8_32x32x16_fp32_adds"):
         assert not results[kind][4], f"{kind} meets the output tolerance: the fp8 GEMM should use it"
+
+
+def test_vendor_fp8_gemm_accuracy(orc):
+    wl = W.WORKLOADS["fp8_16384x4096x12288"]
+    inp = W.make_inputs(wl)
+    qx, s_tok = orc.quantize_fp8(W.bits(inp.x), 0)
+    wq, s_ch = orc.quantize_fp8(W.bits(inp.w), 0)
+    M, K = qx.shape
+    N = wq.shape[0]
+    dev = torch.device("cuda")
+    a8 = torch.from_numpy(qx).to(dev).view(torch.float8_e4m3fn)
+    b8 = torch.from_numpy(wq).to(dev).view(torch.float8_e4m3fn)
+    sa = torch.from_numpy(s_tok).to(dev).view(M, 1).contiguous()
+    sb = torch.from_numpy(s_ch).to(dev).view(1, N).contiguous()
+    try:
+        y = torch._scaled_mm(a8, b8.t(), scale_a=sa, scale_b=sb, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+    except Exception as e:   # no fp8 GEMM with row-wise scales in this torch build
+        pytest.skip(f"torch._scaled_mm with row-wise scales unavailable: {e!r}"[:200])
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(5).choice(M, 30, replace=False)]))
+    y_ref = orc.fp8_gemm_dequant(qx[rows], s_tok[rows], wq, s_ch, None)
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)[rows]
+    max_rel, within = _output_stats(got, y_ref)
+    passes = max_rel <= REL_TOL and within >= ULP_FRAC
+    say(f"  vendor fp8 GEMM ({len(rows)} rows x {N}): output max rel {max_rel:.3e}, within 2 ulp "
+        f"{within:.6f} -> {'passes' if passes else 'fails'} the tolerance")
+    assert within > 0.99, "the vendor fp8 GEMM is far off: check the operand layout of this test"
+    assert not passes, "the vendor fp8 GEMM meets the output tolerance: the fp8 MFMA route should be reconsidered"
