@@ -30,7 +30,7 @@ What each call follows (pages on quantized Clef checkpoints):
 * ``gateup_swiglu_quant`` -- the SwiGLU output handed to the next (down)
   projection as int8 input: the per-token activation quantizer (INT8 ConvRot
   card, latency-table notes) applied to the bf16 output of the paired gate/up
-  epilogue, with the next projection's rotation (reading R7 in the C++ header).
+  epilogue, with the next projection's rotation (reading R17 in the C++ header).
 
 No function here carries a "parity unpinned" mark: each is pinned by the
 ``-m "not gpu"`` tests in ``tests/test_oracle_*.py``.

@@ -35,7 +35,7 @@
 //       to bf16 (round half to even).
 //   R6  SwiGLU: g, u = the unrounded epilogue values of packed rows n and
 //       N + n; output bf16(g * sigmoid(g) * u) evaluated in fp64.
-//   R7  the SwiGLU output handed to the next (down) projection as int8 input:
+//   R17 the SwiGLU output handed to the next (down) projection as int8 input:
 //       that projection's activations go through the same per-token activation
 //       quantizer as every INT8 projection ("CLEF Calibrated INT8 ConvRot"
 //       card, notes under the latency table), applied to the bf16 output of
@@ -467,7 +467,7 @@ void orc_gateup_unfused(const uint16_t* x, const int8_t* w, const float* s_ch, c
   orc_swiglu_bf16(h.data(), h.data() + N, 2 * N, y, M, N, nthreads);
 }
 
-// ---- the SwiGLU output quantized for the next linear (R7) ----
+// ---- the SwiGLU output quantized for the next linear (R17) ----
 // Whole: x -> gate/up SwiGLU (rotation rot_in on x) -> the per-token quantizer of
 // the bf16 SwiGLU output, with the next linear's rotation rot_out: codes q [M, N]
 // and scales s [M].

@@ -9,8 +9,8 @@ computes the contraction four ways -- the fp8 MFMA (32x32x16, chained), the scal
 f8f6f4 MFMA (32x32x64, chained), the fp8 MFMA with every partial sum added in fp32 by
 the VALU, and exact widening to bf16 on the bf16 MFMA (the library's route) -- and
 each is compared with the oracle's exact sums (``orc.gemm_fp8``), then through the
-dequant epilogue with the bf16 output tolerance (max relative error 1e-2 under the
-R10 denominator, 99.9% within 2 bf16 ulps).
+dequant epilogue with the bf16 output tolerance (max relative error 1e-2, the error
+taken relative to max(|ref|, 1e-3 * rms(ref)); 99.9% within 2 bf16 ulps).
 
 Asserted: the bf16 route sums to fp32 accuracy and passes the output tolerance; each
 fp8 MFMA route's error and tolerance outcome is measured and printed, and the

@@ -45,8 +45,9 @@ def test_swiglu_stage(lib, orc, M, N, ld):
 
 def _check(lib, orc, wl, rows=None):
     """Stage by stage, each at the single-rounding tolerance: the projection onto the 2N
-    packed rows against the oracle's, then the SwiGLU against the oracle applied to the
-    GPU's own bf16 projection.  End to end against the oracle's chain the bound is wider:
+    packed rows against the oracle's, then the GPU's SwiGLU pass run on the oracle's
+    projection against the oracle's SwiGLU of it.  End to end against the oracle's chain
+    the bound is wider:
     where the two projections differ by an ulp (an fp32-vs-fp64 near-tie), the SwiGLU
     scales that relative change by |d ln silu(g) / d ln g| = |1 + g (1 - sigmoid(g))|,
     which grows like |g| for very negative gates, so the chain is held to the first-order
@@ -70,7 +71,11 @@ def _check(lib, orc, wl, rows=None):
     h_got = bf16_bits(h)[rows]
     compare_bf16(h_got, h_ref, f"{wl.name} projection onto 2N rows ({len(rows)} rows)")
     y_got = bf16_bits(y)[rows]
-    compare_bf16(y_got, orc.swiglu_bf16(h_got[:, :N], h_got[:, N:]), f"{wl.name} swiglu stage")
+    # the SwiGLU stage on the oracle's projection (uploaded; same row stride as the GPU's)
+    h_ref_d = torch.from_numpy(h_ref.view(np.int16)).view(torch.bfloat16).to(dev)
+    y_stage = lib.w8a8_swiglu(h_ref_d[:, :N], h_ref_d[:, N:])
+    torch.cuda.synchronize()
+    compare_bf16(bf16_bits(y_stage), orc.swiglu_bf16(h_ref[:, :N], h_ref[:, N:]), f"{wl.name} swiglu stage")
     y_ref = orc.gateup_unfused(x_rows, wq_ref, s_ch_ref, bias_bits, wl.rot_block)
     # end to end: first-order propagation of the projection differences through
     # silu(g) * u, plus the final rounding of each side (at most 2 ulp apart)
