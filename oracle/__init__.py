@@ -73,9 +73,15 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
-        build(force=True)
-    lib = ctypes.CDLL(str(_LIB_PATH))
+    # W8A8_ORACLE_LIB: a separately built copy (the mutation tests load copies of the
+    # oracle with a planted mistake, to show that the pins catch it)
+    alt = os.environ.get("W8A8_ORACLE_LIB")
+    if alt:
+        lib = ctypes.CDLL(alt)
+    else:
+        if not _LIB_PATH.exists() or _LIB_PATH.stat().st_mtime < _SRC.stat().st_mtime:
+            build(force=True)
+        lib = ctypes.CDLL(str(_LIB_PATH))
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
     I = ctypes.c_int
