@@ -185,8 +185,8 @@ __device__ __forceinline__ void rotate_chunk(const u32x4 (&raw)[4], int lane, fl
 // blocks.  The 4-point transform across quarters is a matrix product on the fp64
 // matrix core: v_mfma_f64_4x4x4f64 runs 4 independent 4x4x4 products, one per
 // lane group of equal bits 2-3, with B[k][j] = lane 16k + 4b + j, A[i][k] = lane
-// 16k + 4b + i and D[i][j] = lane 16i + 4b + j (b = the group; layout checked by
-// a GPU probe).  B is a value of quarter k of column 4b + j, A = H4, so D at
+// 16k + 4b + i and D[i][j] = lane 16i + 4b + j (b = the group; the layout is
+// checked on the device by tests/test_gpu_f64_mfma_layout.py).  B is a value of quarter k of column 4b + j, A = H4, so D at
 // lane 16q + n is sum_k H4[q][k] * (quarter k of column n): quarter q of the
 // transform, landing in the lane that holds quarter q.  Products with +-1 are
 // exact and the sums are those of the exact block sums, so the result is the

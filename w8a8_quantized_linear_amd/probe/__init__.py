@@ -2,14 +2,16 @@
 W8A8 path and not part of the library's C ABI (``include/w8a8.h``).
 
 ``libw8a8_probe.so`` (built next to this file by ``w8a8_quantized_linear_amd/build.py``)
-holds two kernels:
+holds three kernels:
 
 * ``mfma_rate`` -- the rate the matrix cores sustain with register operands and no
   memory traffic (int8 32x32x32 or bf16 32x32x16 MFMAs): the measured-clock
   ceiling the GEMM is set against (``bench.py --mfma-peak``);
 * ``fp8_contraction`` -- an E4M3FN x E4M3FN contraction through the fp8 matrix
   instructions, or through exact widening to bf16, for measuring how accurately
-  each sums its products.
+  each sums its products;
+* ``f64_mfma_layout`` -- the lane layout of the fp64 4x4x4 matrix instruction that
+  the quantizer's rotation uses.
 """
 from __future__ import annotations
 
@@ -28,6 +30,8 @@ _lib.w8a8_probe_mfma_rate.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int
 _lib.w8a8_probe_fp8_contraction.restype = ctypes.c_int
 _lib.w8a8_probe_fp8_contraction.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+_lib.w8a8_probe_f64_mfma_layout.restype = ctypes.c_int
+_lib.w8a8_probe_f64_mfma_layout.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
 FP8_KINDS = {"fp8_32x32x16": 0, "f8f6f4_32x32x64": 1, "fp8_32x32x16_fp32_adds": 2, "bf16_widened": 3}
 
@@ -65,3 +69,12 @@ def fp8_contraction(kind: str, a: torch.Tensor, b: torch.Tensor) -> torch.Tensor
                                        _stream()) != 0:
         raise RuntimeError("w8a8_probe_fp8_contraction: unsupported shape or launch failure")
     return c
+
+
+def f64_mfma_layout() -> torch.Tensor:
+    """D [64 launches, 64 lanes] of v_mfma_f64_4x4x4f64 with A one-hot at lane L in
+    launch L, B = lane + 1, C = 0 (fp64, on the device)."""
+    out = torch.zeros((64, 64), dtype=torch.float64, device="cuda")
+    if _lib.w8a8_probe_f64_mfma_layout(out.data_ptr(), _stream()) != 0:
+        raise RuntimeError("w8a8_probe_f64_mfma_layout: launch failure")
+    return out
