@@ -17,11 +17,12 @@
 // rows) tile; each wave accumulates a (BM/WGM) x (BN/WGN) sub-tile from 32x32
 // MFMA blocks: v_mfma_i32_32x32x32_i8 for int8; E4M3FN operands are widened
 // exactly to bf16 in registers and go through v_mfma_f32_32x32x16_bf16, because
-// the gfx950 fp8 MFMAs sum groups of products at roughly 14-bit precision
-// (measured: error ~2e-4 of the output rms at K = 4096 whatever the instruction
-// width or accumulator chaining) -- not the fp32 accumulation the fp8 scheme
-// calls for -- while the bf16 MFMA on the same values is accurate to fp32
-// rounding.  The weight fragment is the MFMA's A operand and the token fragment
+// the gfx950 fp8 MFMAs sum their products less accurately than fp32 accumulation
+// (measured on the device by tests/test_gpu_fp8_mfma_accuracy.py: errors up to
+// ~3e-4 of the output rms at K = 4096 for the 32x32x16 and scaled 32x32x64 fp8
+// instructions, chained or with fp32 partial sums, which fails the bf16 output
+// tolerance on outputs near zero), while the bf16 MFMA on the same values is
+// accurate to fp32 rounding.  The weight fragment is the MFMA's A operand and the token fragment
 // its B operand, so a lane ends up holding four consecutive output columns of
 // one token row.
 //
