@@ -301,11 +301,17 @@ def vendor_gemm(torch, W, lib, names, launches=20):
         torch.cuda.empty_cache()
 
 
+def traffic_key(workload: str, path: str) -> str:
+    """Name of the stored counter record of a workload's GEMM on a bench path."""
+    return workload + ("-unfused" if path == "unfused" else "") + ("-swiglu-quant" if path == "swiglu-quant" else "")
+
+
 def main():
     args = parse()
     if args.pmc_summary:
-        rec = pmc_summary(args.workload, *args.pmc_summary)
-        out = ROOT / "profiles" / f"traffic_{args.workload}.json"
+        key = traffic_key(args.workload, args.path)
+        rec = pmc_summary(key, *args.pmc_summary)
+        out = ROOT / "profiles" / f"traffic_{key}.json"
         out.write_text(json.dumps(rec, indent=1) + "\n")
         print(json.dumps(rec, indent=1))
         return
@@ -496,8 +502,7 @@ def main():
     g_bytes = M * K + Nw * K + 4 * (M + Nw) + out_bytes + (0 if bias0 is None else 2 * Nw)
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
     # (a stored record covers the GEMM kernel alone, not the single whole-path call)
-    traffic = None if single else stored_traffic(wl.name + ("-unfused" if unfused else "")
-                                                 + ("-swiglu-quant" if quantout else ""))
+    traffic = None if single else stored_traffic(traffic_key(wl.name, args.path))
 
     out = {
         "metric": "W8A8 linear TOPS incl. quant+dequant, % int8 MFMA peak; quantizer GB/s",
