@@ -187,3 +187,32 @@ def test_gateup_full_size_with_down_rotation(lib, orc):
     h_ref = orc.gateup_swiglu(x_rows, wq_ref, s_ch_ref, None, 0)
     _check_against_oracle(orc, q_gpu, s_gpu, h_gpu, h_ref, x_rows, wq_ref, s_ch_ref, None, 0, 128,
                           f"full size, {len(rows)} rows")
+
+
+def test_codes_feed_the_down_projection(lib, orc):
+    """The packed codes and scales are the down projection's A operand as they stand:
+    w8a8_gemm_dequant_packed on them (K = N) against the oracle's chain (SwiGLU output
+    quantized per token, then the down projection's GEMM and dequant), on the rows whose
+    SwiGLU output equals the oracle's (the same codes, so the outputs within the bf16
+    tolerance)."""
+    M, K, N, N2 = 300, 256, 384, 264
+    wl = W.custom("gateup", M, K, N, 0, bias=True, seed=123)
+    inp, wq, s_ch, wp, s_ch_d, bias, bias_bits = _setup(lib, orc, wl)
+    dev = torch.device("cuda")
+    down = W.custom("linear", M, N, N2, 128, bias=True, seed=124)
+    dinp = W.make_inputs(down)
+    w2q, s2_ch = orc.quantize_i8(W.bits(dinp.w), 128)
+    ws = torch.empty(lib.swiglu_quant_workspace_bytes(M, N, K), dtype=torch.uint8, device=dev)
+    q, s = lib.w8a8_gateup_swiglu_quant_packed(inp.x.to(dev), wp, N, s_ch_d, bias, rot_in=0, rot_out=128,
+                                               workspace=ws)
+    y2 = lib.w8a8_gemm_dequant_packed(q, s, lib.w8a8_pack_weight(torch.from_numpy(w2q).to(dev)),
+                                      torch.from_numpy(s2_ch).to(dev), N, bias=dinp.bias.to(dev))
+    torch.cuda.synchronize()
+    x_bits = W.bits(inp.x)
+    h_ref = orc.gateup_swiglu(x_bits, wq, s_ch, bias_bits, 0)
+    q_o, s_o = orc.gateup_swiglu_quant(x_bits, wq, s_ch, bias_bits, 0, 128)
+    y2_ref = orc.gemm_dequant(q_o, s_o, w2q, s2_ch, W.bits(dinp.bias))
+    eq = np.all(bf16_bits(lib.swiglu_quant_h(ws, M, N, K)) == h_ref, axis=1)
+    say(f"  down projection on the SwiGLU output's codes: {int(eq.sum())} of {M} rows with equal h")
+    assert eq.sum() >= M // 2
+    compare_bf16(bf16_bits(y2)[eq], y2_ref[eq], "down projection outputs")
