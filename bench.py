@@ -75,6 +75,10 @@ def parse():
                          "the GPU raises its clock over the first tens of milliseconds of sustained "
                          "load, and steps timed before that run up to 13%% slow)")
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--shard", type=int, default=1, metavar="P",
+                    help="time one GPU's share of the workload split P ways, on this one GPU: token "
+                         "rows (ceil(M / P)) for the linear and fp8 workloads, output columns (N / P of "
+                         "each of gate and up, so the SwiGLU stays local) for gate/up; nothing else changes")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--path", choices=("fused", "unfused", "single", "swiglu-quant"),
                     default="fused",
@@ -349,6 +353,17 @@ def main():
         return
 
     wl = W.WORKLOADS[args.workload]
+    if args.shard > 1:
+        import dataclasses
+        P = args.shard
+        if wl.kind == "gateup":
+            if wl.N % (8 * P):
+                print(f"bench.py: N = {wl.N} does not split into {P} column shards of a multiple of 8",
+                      file=sys.stderr)
+                sys.exit(2)
+            wl = dataclasses.replace(wl, N=wl.N // P, name=f"{wl.name}-columns-1of{P}")
+        else:
+            wl = dataclasses.replace(wl, M=-(-wl.M // P), name=f"{wl.name}-rows-1of{P}")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     # untimed elementwise kernel of known size (reads and writes CALIBRATION_BYTES):
@@ -521,7 +536,8 @@ def main():
                    "rot_block": wl.rot_block,
                    "path": wl.kind + ("-unfused" if unfused else "") + ("-single-call" if single else "")
                    + (f"-{args.path}-rot{args.rot_out}" if quantout else ""),
-                   "parallelism": "single GPU",
+                   "parallelism": "single GPU" if args.shard == 1 else
+                   f"one GPU's share of {args.shard} ({'gate/up columns' if wl.kind == 'gateup' else 'token rows'})",
                    "operand_copies": copies, "clock_ramp_steps": ramp},
         "pct_of_peak": 100.0 * ops / (ms_per_step * 1e-3) / (peak * 1e12),
         "roofline": {"bound": "mfma", "achieved": ops / tg / 1e12, "peak": peak, "unit": "TFLOP/s",
