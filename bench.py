@@ -96,6 +96,12 @@ def parse():
                     help="instead of the workload: the rate the matrix cores sustain with register "
                          "operands and no memory traffic (int8 32x32x32 and bf16 32x32x16 MFMAs), "
                          "after a ramp-up launch -- the measured-clock ceiling for the GEMM")
+    ap.add_argument("--stream-peak", action="store_true",
+                    help="instead of the workload line: on each workload's activation shape, the HBM "
+                         "rate of a kernel with the quantizer's traffic and no arithmetic (2 bytes read, "
+                         "1 written per element), of a plain bf16 copy, and of the library's quantizer "
+                         "itself, event-timed in one process after a clock ramp -- the achievable "
+                         "streaming ceiling the quantizer is set against")
     ap.add_argument("--vendor-gemm", action="store_true",
                     help="instead of the workload line: the vendor library's GEMM on each large workload's "
                          "shape (hipBLASLt through torch: torch._int_mm, int8 -> int32, for the int8 "
@@ -249,6 +255,61 @@ def mfma_peak(torch, blocks=768, launch_s=0.2):
     return out
 
 
+def stream_peak(torch, W, lib, names, launches=50):
+    """Achievable streaming rate next to the quantizer, per activation shape: the
+    bench-only streaming probe (bf16 -> one byte per element; bf16 copy) and the
+    library's quantizer (packed codes), each cycling through enough input/output
+    copies that the last-level cache cannot serve them, after a clock ramp; median of
+    three timed runs of `launches` back-to-back launches."""
+    import statistics
+    import w8a8_quantized_linear_amd.probe as probe
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream().cuda_stream
+    for name in names:
+        wl = W.WORKLOADS[name]
+        M, K = wl.M, wl.K
+        fp8 = wl.kind == "fp8"
+        x0 = W.make_inputs(wl).x.to(dev)
+        copies = max(2, -(-ROTATION_BYTES // (5 * M * K)))
+        xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+        ys = [torch.empty((2 * M * K,), dtype=torch.uint8, device=dev) for _ in range(copies)]
+        qs = [torch.empty((lib.packed_bytes(M, K),), dtype=torch.uint8, device=dev) for _ in range(copies)]
+        ss = [torch.empty((M,), dtype=torch.float32, device=dev) for _ in range(copies)]
+        qfn = lib._lib.w8a8_quantize_act_fp8_packed if fp8 else lib._lib.w8a8_quantize_act_packed
+
+        def quantize(i):
+            st = qfn(xs[i].data_ptr(), M, K, wl.rot_block, qs[i].data_ptr(), ss[i].data_ptr(), stream)
+            if st != 0:
+                raise RuntimeError(f"quantizer: status {st}")
+        runs = {"probe_bf16_to_byte": (3 * M * K, lambda i: probe.stream("bf16_to_byte", xs[i], ys[i])),
+                "probe_copy": (4 * M * K, lambda i: probe.stream("copy", xs[i], ys[i])),
+                "quantizer": (3 * M * K + 4 * M, quantize)}
+        t = time.perf_counter()
+        i = 0
+        while time.perf_counter() - t < RAMP_SECONDS:   # clock ramp, untimed
+            for _, fn in runs.values():
+                fn(i % copies)
+            i += 1
+            torch.cuda.synchronize()
+        rec = {"stream_peak": name, "M": M, "K": K, "rot_block": wl.rot_block, "codes": "e4m3fn" if fp8 else "int8"}
+        for key, (nbytes, fn) in runs.items():
+            us = []
+            for _ in range(3):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                for j in range(launches):
+                    fn(j % copies)
+                e1.record()
+                torch.cuda.synchronize()
+                us.append(e0.elapsed_time(e1) / launches * 1e3)
+            u = statistics.median(us)
+            rec[key] = {"us": u, "bytes": nbytes, "gbs": nbytes / u / 1e3, "frac_of_8tbs": nbytes / u / 1e3 / PEAK_HBM_GBS}
+        rec["quantizer_vs_probe"] = rec["quantizer"]["gbs"] / rec["probe_bf16_to_byte"]["gbs"]
+        print(json.dumps(rec), flush=True)
+        del xs, ys, qs, ss, x0
+        torch.cuda.empty_cache()
+
+
 def vendor_gemm(torch, W, lib, names, launches=20):
     """Per-launch time of the vendor GEMM and of this library's GEMM on the same codes."""
     dev = torch.device("cuda:0")
@@ -334,6 +395,9 @@ def main():
         return
     if args.vendor_gemm:
         vendor_gemm(torch, W, lib, [n for n in W.ORDER if W.WORKLOADS[n].M >= 2048])
+        return
+    if args.stream_peak:
+        stream_peak(torch, W, lib, [n for n in W.ORDER if W.WORKLOADS[n].M >= 2048])
         return
     if args.drift:
         import numpy as np

@@ -288,3 +288,7 @@ def test_probe_argument_checks():
     assert c(0, A, A, A, 32, 32, 96, None) == -1      # K % 64
     assert c(5, A, A, A, 32, 32, 64, None) == -1      # kind
     assert c(0, None, A, A, 32, 32, 64, None) == -1
+    pl.w8a8_probe_stream.restype, pl.w8a8_probe_stream.argtypes = I, [I, P, P, I64, P]
+    st = pl.w8a8_probe_stream
+    assert st(2, A, A, 8, None) == -1 and st(0, None, A, 8, None) == -1 and st(1, A, None, 8, None) == -1
+    assert st(0, A, A, 0, None) == -1 and st(0, A, A, -1, None) == -1

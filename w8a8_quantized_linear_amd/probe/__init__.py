@@ -11,7 +11,10 @@ holds three kernels:
   instructions, or through exact widening to bf16, for measuring how accurately
   each sums its products;
 * ``f64_mfma_layout`` -- the lane layout of the fp64 4x4x4 matrix instruction that
-  the quantizer's rotation uses.
+  the quantizer's rotation uses;
+* ``stream`` -- the HBM rate of a kernel with the quantizer's traffic (2 bytes read,
+  1 byte written per element) and no arithmetic, or of a plain copy: the achievable
+  streaming ceiling the quantizer is set against (``bench.py --stream-peak``).
 """
 from __future__ import annotations
 
@@ -32,6 +35,8 @@ _lib.w8a8_probe_fp8_contraction.argtypes = [ctypes.c_int, ctypes.c_void_p, ctype
                                             ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
 _lib.w8a8_probe_f64_mfma_layout.restype = ctypes.c_int
 _lib.w8a8_probe_f64_mfma_layout.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+_lib.w8a8_probe_stream.restype = ctypes.c_int
+_lib.w8a8_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
 
 FP8_KINDS = {"fp8_32x32x16": 0, "f8f6f4_32x32x64": 1, "fp8_32x32x16_fp32_adds": 2, "bf16_widened": 3}
 
@@ -78,3 +83,22 @@ def f64_mfma_layout() -> torch.Tensor:
     if _lib.w8a8_probe_f64_mfma_layout(out.data_ptr(), _stream()) != 0:
         raise RuntimeError("w8a8_probe_f64_mfma_layout: launch failure")
     return out
+
+
+STREAM_KINDS = {"bf16_to_byte": 0, "copy": 1}
+
+
+def stream(kind: str, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
+    """One launch of the streaming probe on the current stream.  x: contiguous bf16
+    device tensor whose element count is a multiple of 8; y: contiguous device tensor
+    of at least numel(x) bytes ("bf16_to_byte": the high byte of each element) or
+    2 * numel(x) bytes ("copy")."""
+    k = STREAM_KINDS[kind]
+    if x.dtype != torch.bfloat16 or not x.is_cuda or not x.is_contiguous() or x.numel() % 8 != 0 or x.numel() == 0:
+        raise ValueError("x: a contiguous bf16 device tensor, a positive multiple of 8 elements")
+    need = x.numel() * (1 if k == 0 else 2)
+    if not y.is_cuda or not y.is_contiguous() or y.numel() * y.element_size() < need or y.device != x.device:
+        raise ValueError(f"y: a contiguous device tensor of at least {need} bytes on x's device")
+    if _lib.w8a8_probe_stream(k, x.data_ptr(), y.data_ptr(), x.numel() // 8, _stream()) != 0:
+        raise RuntimeError("w8a8_probe_stream: bad argument or launch failure")
+    return y
