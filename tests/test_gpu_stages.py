@@ -108,12 +108,15 @@ def _tile_choice(M, N):
 
 
 # One shape per tile the launcher picks, at the workloads' depths (K = 5,120 and
-# 17,408: long K loops over the 4-stage ring), in both operand layouts.
-TILE_SHAPES = [(300, 264, 512, "128x128"), (1502, 4096, 5120, "192x128"), (2048, 8192, 17408, "256x256")]
+# 17,408: long K loops over the 4-stage ring), in both operand layouts; the last
+# runs the persistent 256 x 256 form with two tiles per workgroup, ragged in M and N.
+TILE_SHAPES = [(300, 264, 512, "128x128"), (1502, 4096, 5120, "192x128"), (2048, 8192, 17408, "256x256"),
+               (4000, 8136, 1024, "256x256")]
 
 
 @pytest.mark.parametrize("packed", [False, True], ids=["row-major", "packed"])
-@pytest.mark.parametrize("M,N,K,tile", TILE_SHAPES, ids=[t[3] for t in TILE_SHAPES])
+@pytest.mark.parametrize("M,N,K,tile", TILE_SHAPES, ids=[t[3] + ("-2-per-workgroup" if t[0] == 4000 else "")
+                                                          for t in TILE_SHAPES])
 def test_gemm_i32_exact_on_every_tile(lib, orc, M, N, K, tile, packed):
     """int32 accumulators bit for bit against the oracle's integer GEMM, on the tile
     shapes and K loops the workloads run (the dequant and SwiGLU epilogues read exactly
@@ -282,10 +285,16 @@ def test_quantize_packed(lib, orc, fp8, M, K, rot):
 
 
 @pytest.mark.parametrize("kind", ["dequant", "swiglu", "fp8"])
-@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (130, 136, 256), (1099, 4088, 256), (2047, 4088, 384)])
+@pytest.mark.parametrize("M,N,K", [(1, 8, 128), (130, 136, 256), (1099, 4088, 256), (2047, 4088, 384),
+                                   (4000, 8136, 256)])
 def test_gemm_stages_on_packed_operands(lib, orc, kind, M, N, K):
     """Packed activation codes x packed weight codes through the *_packed GEMM entry
-    points, against the oracle (tile configurations 128, 192 and 256 all run)."""
+    points, against the oracle (tile configurations 128, 192 and 256 all run).  The
+    last shape runs the persistent 256 x 256 form with 2 tiles per workgroup (4 for
+    SwiGLU: 1,024 tiles of 128 output columns), ragged in M and N, so every workgroup
+    carries its operand ring, scales and bias from one tile into the next."""
+    if (M, N) == (4000, 8136):
+        assert _tile_choice(M, 2 * N if kind == "swiglu" else N) == "256x256"
     say(f"packed gemm {kind} M={M} N={N} K={K}")
     Nw = 2 * N if kind == "swiglu" else N
     if kind == "fp8":

@@ -40,6 +40,14 @@
 // with its own L2), so block ids are remapped to give every XCD a contiguous
 // range of tiles, walked in groups of kGroupM token tiles so that concurrently
 // running tiles on one XCD share their token and weight panels in its L2.
+//
+// The 256 x 256 tile (one workgroup per CU) runs persistent (gemm_persist):
+// each workgroup walks several tiles and its operand ring runs on from one tile
+// into the next, so the next tile's first stages load while this tile's
+// epilogue runs; the smaller tiles (two workgroups per CU) launch one
+// workgroup per tile (gemm_tile), where one workgroup's epilogue overlaps the
+// other's K loop.
+#include <algorithm>
 #include <type_traits>
 
 #include "epilogue_math.h"
@@ -500,6 +508,402 @@ hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const fl
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Persistent form of the 256 x 256 tile (one workgroup per CU, walking the
+// tiles of its XCD's range, P workgroups per XCD taking every P-th tile, so the
+// tiles running at once on an XCD are the same as in a one-tile-per-workgroup
+// launch).  Launched one tile per workgroup, every CU would finish its K loop
+// at the same moment, write its output and then fetch the next tile's first
+// stages, all CUs together: ~12 us per round of tiles measured at
+// 12,016 x 5,120 x K (the intercept of the launch time against K).  Here the
+// operand ring runs on from one tile into the next: the next tile's first
+// stages are issued during this tile's last stages and land while its epilogue
+// runs.  The epilogue therefore cannot stage its output in the ring: each wave
+// stages 32 rows x half its columns at a time in an LDS area of its own, and
+// the tile's token scales, channel scales and bias come into LDS by
+// direct-to-LDS loads at the start of the tile (two areas, by tile parity, so
+// the next tile's scales never overwrite ones a wave still reads).  Outputs go
+// out as buffer stores, whose out-of-range lanes the hardware drops, so every
+// wave issues the same number of stores and the vector-memory counts stay
+// exact.  Wait counts (loads and stores complete in issue order): in the first
+// two stages of every tile after the first, the epilogue's stores and the
+// scale loads were issued after the stage being waited for.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void lds_dma4(const void* g, uint8_t* l) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+#endif
+}
+
+}  // namespace
+}  // namespace w8a8
+__device__ void w8a8_raw_buffer_store_x4(w8a8::i32x4 vdata, w8a8::i32x4 rsrc, int voffset, int soffset,
+                                          int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
+namespace w8a8 {
+namespace {
+
+// (tile index within the launch) -> (tile_m, tile_n), walked in groups of kGroupM token tiles
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupM * tiles_n;
+  const int group = t / per_group, first_m = group * kGroupM;
+  const int gsize = min(kGroupM, tiles_m - first_m);
+  const int in = t % per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any persistent launch's output
+
+template <Epi EPI, bool FP8, bool PA, bool PB>
+__global__ void __launch_bounds__(256)
+gemm_persist(const uint8_t* __restrict__ a, const float* __restrict__ s_tok,
+             const uint8_t* __restrict__ b, const float* __restrict__ s_ch,
+             const uint16_t* __restrict__ bias, void* __restrict__ out,
+             int64_t M, int64_t N, int64_t K, int tiles_m, int tiles_n) {
+  constexpr int BM = 256, BN = 256, WGM = 2, WGN = 2, BK = 64, NST = 4;
+  constexpr int NT = 256;
+  constexpr int CH = BK / 16;
+  constexpr int NSUB = BK / 32;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int TM = WTM / 32, TN = WTN / 32;
+  constexpr int A_LOADS = BM * CH / NT, B_LOADS = BN * CH / NT;
+  constexpr int A_BYTES = BM * BK, B_BYTES = BN * BK, STAGE = A_BYTES + B_BYTES;
+  constexpr int LOADS = A_LOADS + B_LOADS;
+  constexpr bool kPair = paired_epi(EPI);
+  constexpr bool kRaw = EPI == Epi::kRawI32;
+  constexpr int COLS = kPair ? WTN / 2 : WTN;   // output columns of a wave's sub-tile
+  constexpr int HALF = COLS / 2;                // columns staged at a time
+  constexpr int TNO = COLS / 32, TNH = TNO / 2; // 32-column output blocks (per half)
+  constexpr int ROWB = HALF * 2;                // bytes per staged row
+  constexpr int CPR = ROWB / 16;                // 16-byte chunks per staged row
+  constexpr int RPI = 64 / CPR;                 // staged rows per store instruction
+  constexpr int SREG = 32 * ROWB;               // staging bytes per wave
+  constexpr int RING = NST * STAGE;
+  constexpr int SC_BYTES = 3 * 1024;            // s_tok[256] f32, s_ch[256] f32, bias 4 x 256 B
+  constexpr int D = kRaw ? 0 : 3;                // scale / bias loads per wave per tile (the raw
+                                                // int32 epilogue has no scales: its pointers are null)
+  constexpr int S = kRaw ? 0 : TM * 2 * (32 / RPI);  // output stores per wave per tile (raw: counted as 0)
+  constexpr int N0 = (NST - 3) * LOADS, N1 = N0 + S + D;
+  static_assert(CPR == 4 || CPR == 8, "staged rows of 4 or 8 chunks");
+  static_assert(N1 < 64, "vmcnt range");
+  static_assert(!kPair || (BN / 2) % (NT / CH) == 0, "each load instruction reads gate rows only or up rows only");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[RING + 4 * SREG + 2 * SC_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave % WGM, wn = wave / WGM;
+  const int frag_row = lane & 31, frag_half = lane >> 5;
+
+  // this workgroup's tiles: XCD x's contiguous range, every per_xcd-th from idx
+  const int ntiles = tiles_m * tiles_n;
+  const int per_xcd = gridDim.x / kXcds;
+  const int xcd = blockIdx.x % kXcds, idx = blockIdx.x / kXcds;
+  const int q8 = ntiles / kXcds, r8 = ntiles % kXcds;
+  const int t_first = xcd * q8 + min(xcd, r8);
+  const int t_count = q8 + (xcd < r8 ? 1 : 0);
+  if (idx >= t_count) return;
+  const int64_t ksteps = K / BK;
+
+  auto tile_mb = [&](int t) -> int64_t { int tm, tn; tile_coords(t, tiles_m, tiles_n, tm, tn); return (int64_t)tm * BM; };
+  auto tile_nb = [&](int t) -> int64_t {
+    int tm, tn; tile_coords(t, tiles_m, tiles_n, tm, tn);
+    return kPair ? (int64_t)tn * (BN / 2) : (int64_t)tn * BN;
+  };
+
+  // ---- issue side: the tile and k of the next stage to load, its panels and offsets
+  auto src_off = [&](int64_t rel, int c, bool packed) -> uint32_t {
+    if (packed)
+      return (uint32_t)((rel / 32) * 32 * K + (rel % 32) * 64 + (c / 4) * 2048 + (c % 4) * 16);
+    return (uint32_t)(rel * K + c * 16);
+  };
+  constexpr int ROWS_PER_LOAD = NT / CH;
+  int it_i = idx;                 // position of the issue tile in this XCD's range
+  int64_t it_k = 0;               // next stage of the issue tile
+  const uint8_t* a_panel;
+  const uint8_t* b_panel;
+  const uint8_t* b_up_panel;
+  uint32_t a_off[A_LOADS], b_off[B_LOADS];
+  auto set_issue_tile = [&](int t) __attribute__((always_inline)) {
+    const int64_t mb = tile_mb(t), nb = tile_nb(t);
+    a_panel = a + mb * K;
+    const int64_t up_first = N + nb;
+    const int64_t up_base = PB ? up_first / 32 * 32 : up_first;
+    const int64_t up_skew = up_first - up_base;
+    b_panel = b + nb * K;
+    b_up_panel = b + up_base * K;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
+      a_off[i] = src_off(min<int64_t>(r, M - 1 - mb), c, PA);
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int p = i * NT + tid, r = p / CH, c = (p % CH) ^ swz_key<CH>(r);
+      if constexpr (kPair) {
+        const int64_t col = min<int64_t>(r % (BN / 2), N - 1 - nb);
+        b_off[i] = src_off(r < BN / 2 ? col : up_skew + col, c, PB);
+      } else {
+        b_off[i] = src_off(min<int64_t>(r, N - 1 - nb), c, PB);
+      }
+    }
+  };
+  set_issue_tile(t_first + it_i);
+  // Before each issue: past the issue tile's last stage move on to the next tile
+  // of this workgroup; past the last tile keep re-loading its last stage (those
+  // buffers are never multiplied; every stage issues the same loads).
+  auto advance_issue = [&]() __attribute__((always_inline)) {
+    if (it_k == ksteps) {
+      if (it_i + per_xcd < t_count) {
+        it_i += per_xcd;
+        it_k = 0;
+        set_issue_tile(t_first + it_i);
+      } else {
+        it_k = ksteps - 1;
+      }
+    }
+  };
+  int64_t g_issue = 0;  // global stage index of the next issue (ring buffer g % NST)
+  auto issue = [&]() __attribute__((always_inline)) {
+    const uint32_t ks = (uint32_t)it_k;
+    const uint32_t ka = PA ? ks * (BK / 64) * 2048 : ks * BK;
+    const uint32_t kb = PB ? ks * (BK / 64) * 2048 : ks * BK;
+    uint8_t* st = lds + (int)(g_issue % NST) * STAGE;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) lds_dma16(a_panel + (a_off[i] + ka), st + (i * NT + wave * 64) * 16);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const bool up = kPair && i * ROWS_PER_LOAD >= BN / 2;
+      lds_dma16((up ? b_up_panel : b_panel) + (b_off[i] + kb), st + A_BYTES + (i * NT + wave * 64) * 16);
+    }
+    ++g_issue;
+    ++it_k;
+  };
+
+  // ---- scales and bias of a tile into LDS area (j & 1): wave w loads token rows
+  // 64w.., channel columns 64w.. of the tile's 256 weight rows (gate rows then up
+  // rows when paired), and bias pairs for those columns into its own 256-byte window
+  const bool has_bias = bias != nullptr;
+  auto load_scales = [&](int t, int j) __attribute__((always_inline)) {
+    uint8_t* area = lds + RING + 4 * SREG + (j & 1) * SC_BYTES;
+    const int64_t mb = tile_mb(t), nb = tile_nb(t);
+    const int64_t m = min<int64_t>(mb + 64 * wave + lane, M - 1);
+    lds_dma4(s_tok + m, area + wave * 256);
+    const int c = 64 * wave + lane;  // local weight row of the tile
+    int64_t n;
+    if constexpr (kPair) n = c < BN / 2 ? min<int64_t>(nb + c, N - 1) : N + min<int64_t>(nb + c - BN / 2, N - 1);
+    else n = min<int64_t>(nb + c, N - 1);
+    lds_dma4(s_ch + n, area + 1024 + wave * 256);
+    const int cp = 64 * wave + 2 * (lane & 31);  // first local row of the lane's bias pair
+    int64_t nbp;
+    if constexpr (kPair) nbp = cp < BN / 2 ? min<int64_t>(nb + cp, N - 2) : N + min<int64_t>(nb + cp - BN / 2, N - 2);
+    else nbp = min<int64_t>(nb + cp, N - 2);
+    const void* bsrc = has_bias ? static_cast<const void*>(bias + nbp) : static_cast<const void*>(s_ch + n);
+    lds_dma4(bsrc, area + 2048 + wave * 256);
+  };
+
+  using Acc = typename std::conditional<FP8, v16f, v16i>::type;
+  Acc acc[TN][TM];
+#pragma unroll
+  for (int i = 0; i < TN; ++i)
+#pragma unroll
+    for (int jj = 0; jj < TM; ++jj) acc[i][jj] = Acc{};
+
+  int a_rows[TM], b_rows[TN];
+#pragma unroll
+  for (int t = 0; t < TM; ++t) a_rows[t] = wm * WTM + t * 32 + frag_row;
+#pragma unroll
+  for (int t = 0; t < TN; ++t) {
+    if constexpr (kPair)
+      b_rows[t] = (t < TN / 2 ? 0 : BN / 2) + wn * (WTN / 2) + (t % (TN / 2)) * 32 + frag_row;
+    else
+      b_rows[t] = wn * WTN + t * 32 + frag_row;
+  }
+  v4i fa[2 * NSUB][TM], fb[2 * NSUB][TN];
+  auto read_frags = [&](auto set_c, int64_t g, int sub) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    const uint8_t* la = lds + (int)(g % NST) * STAGE;
+    const uint8_t* lb = la + A_BYTES;
+    const int c = 2 * sub + frag_half;
+#pragma unroll
+    for (int t = 0; t < TM; ++t) fa[set][t] = *reinterpret_cast<const v4i*>(la + swz<CH>(a_rows[t], c));
+#pragma unroll
+    for (int t = 0; t < TN; ++t) fb[set][t] = *reinterpret_cast<const v4i*>(lb + swz<CH>(b_rows[t], c));
+  };
+  auto mfmas = [&](auto set_c) __attribute__((always_inline)) {
+    constexpr int set = decltype(set_c)::value;
+    if constexpr (FP8) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        v8bf ca[TM];
+#pragma unroll
+        for (int t = 0; t < TM; ++t)
+          ca[t] = e4m3x8_to_bf16(u32x2{(unsigned)fa[set][t][2 * jj], (unsigned)fa[set][t][2 * jj + 1]});
+#pragma unroll
+        for (int tn = 0; tn < TN; ++tn) {
+          const v8bf cb = e4m3x8_to_bf16(u32x2{(unsigned)fb[set][tn][2 * jj], (unsigned)fb[set][tn][2 * jj + 1]});
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+            acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb, ca[tm], acc[tn][tm], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm)
+          acc[tn][tm] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fb[set][tn], fa[set][tm], acc[tn][tm], 0, 0, 0);
+    }
+  };
+
+  // ---- the tile's epilogue (compute-side tile t, scale area j & 1)
+  const i32x4 out_rsrc = {__builtin_amdgcn_readfirstlane((int)(uint32_t)reinterpret_cast<uint64_t>(out)),
+                          __builtin_amdgcn_readfirstlane((int)(uint32_t)(reinterpret_cast<uint64_t>(out) >> 32)),
+                          __builtin_amdgcn_readfirstlane((int)(uint32_t)(M * N * 2)), 0x00020000};
+  auto epilogue = [&](int t, int j) __attribute__((always_inline)) {
+    const int64_t mb = tile_mb(t), nb = tile_nb(t);
+    if constexpr (kRaw) {
+      store_tile_i32<TM, TN, WTM, WTN>(acc, static_cast<int32_t*>(out), M, N, mb, nb, wm, wn, frag_row, frag_half);
+    } else {
+      const uint8_t* area = lds + RING + 4 * SREG + (j & 1) * SC_BYTES;
+      const float* st_l = reinterpret_cast<const float*>(area);
+      const float* sc_l = reinterpret_cast<const float*>(area + 1024);
+      const uint8_t* bi_l = area + 2048;
+      uint8_t* region = lds + RING + wave * SREG;
+      const int64_t m0 = mb + (int64_t)wm * WTM, n0w = nb + (int64_t)wn * COLS;
+      const int lc0 = wn * COLS;  // the wave's first output column within the tile
+      auto bias4 = [&](int lc, float* f) __attribute__((always_inline)) {  // local weight row lc, 4 values
+        if (has_bias) bf16x4(*reinterpret_cast<const uint2*>(bi_l + (lc / 64) * 256 + (lc % 64) * 2), f);
+        else f[0] = f[1] = f[2] = f[3] = 0.0f;
+      };
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) {
+        const float st = st_l[wm * WTM + tm * 32 + frag_row];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+#pragma unroll
+          for (int tnh = 0; tnh < TNH; ++tnh) {
+            const int tn = h * TNH + tnh;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int nl = tn * 32 + 8 * q + 4 * frag_half;  // column within the wave's sub-tile
+              const int lc = lc0 + nl;
+              const float4 sg = *reinterpret_cast<const float4*>(sc_l + lc);
+              const float sgv[4] = {sg.x, sg.y, sg.z, sg.w};
+              float bg[4], y[4];
+              bias4(lc, bg);
+              if constexpr (!kPair) {
+#pragma unroll
+                for (int v = 0; v < 4; ++v) y[v] = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
+              } else {
+                const float4 su = *reinterpret_cast<const float4*>(sc_l + BN / 2 + lc);
+                const float suv[4] = {su.x, su.y, su.z, su.w};
+                float bu[4];
+                bias4(BN / 2 + lc, bu);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                  const float gv = __builtin_fmaf((float)acc[tn][tm][4 * q + v], st * sgv[v], bg[v]);
+                  const float uv = __builtin_fmaf((float)acc[tn + TN / 2][tm][4 * q + v], st * suv[v], bu[v]);
+                  y[v] = silu_f32(gv) * uv;
+                }
+              }
+              const uint2 hv = make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
+              const int chunk = (nl - h * HALF) / 8;
+              *reinterpret_cast<uint2*>(region + frag_row * ROWB + ((chunk ^ (frag_row % CPR)) * 16) + 8 * frag_half) = hv;
+            }
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+          __builtin_amdgcn_wave_barrier();
+          const int c = lane % CPR;
+#pragma unroll
+          for (int r0 = 0; r0 < 32; r0 += RPI) {
+            const int row = r0 + lane / CPR;
+            const int64_t m = m0 + tm * 32 + row, n = n0w + h * HALF + c * 8;
+            const u32x4 v = *reinterpret_cast<const u32x4*>(region + row * ROWB + ((c ^ (row % CPR)) * 16));
+            const uint32_t off = (m < M && n < N) ? (uint32_t)((m * N + n) * 2) : kOutOfRange;
+            w8a8_raw_buffer_store_x4(i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w}, out_rsrc, (int)off, 0, 2);
+          }
+          __builtin_amdgcn_s_waitcnt(0xc07f);  // the reads are done before the region is rewritten
+          __builtin_amdgcn_wave_barrier();
+        }
+      }
+    }
+  };
+
+  constexpr int NMFMA = TM * TN * (FP8 ? 2 : 1);
+  constexpr int NREAD = TM + TN;
+  constexpr int RD_PER = (NREAD + NMFMA - 1) / NMFMA;
+  constexpr int MEM_PER = (NREAD + LOADS + NMFMA - 1) / NMFMA;
+
+  // prologue: the first tile's scales, then its first NST - 1 stages
+  int j = 0;                 // tiles done by this workgroup
+  int c_i = idx;             // position of the compute tile in this XCD's range
+  if constexpr (!kRaw) load_scales(t_first + c_i, 0);
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s) { advance_issue(); issue(); }
+  wait_vmcnt<(NST - 2) * LOADS>();
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  int64_t g = 0;  // global stage index being multiplied
+  static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
+    read_frags(std::integral_constant<int, decltype(j_c)::value>{}, 0, decltype(j_c)::value);
+  });
+  while (true) {
+    for (int64_t ks = 0; ks < ksteps; ks += 2) {
+      const bool first_pair = ks == 0 && j > 0;
+      static_for<0, 2>([&](auto p_c) __attribute__((always_inline)) {
+        constexpr int p = decltype(p_c)::value;
+        advance_issue();
+        if (first_pair) wait_vmcnt<N1>();
+        else wait_vmcnt<N0>();
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+        static_for<0, NSUB>([&](auto j_c) __attribute__((always_inline)) {
+          constexpr int jj = decltype(j_c)::value;
+          if constexpr (jj == 0) issue();
+          read_frags(std::integral_constant<int, (1 - p) * NSUB + jj>{}, g + 1, jj);
+          mfmas(std::integral_constant<int, p * NSUB + jj>{});
+#pragma unroll
+          for (int i = 0; i < NMFMA; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, jj);
+            __builtin_amdgcn_sched_group_barrier(jj == 0 ? 0x120 : 0x100, jj == 0 ? MEM_PER : RD_PER, jj);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        });
+        ++g;
+      });
+    }
+    epilogue(t_first + c_i, j);
+    ++j;
+    c_i += per_xcd;
+    if (c_i >= t_count) break;
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+      for (int jj = 0; jj < TM; ++jj) acc[i][jj] = Acc{};
+    if constexpr (!kRaw) load_scales(t_first + c_i, j);
+  }
+  // every load into LDS has landed before the workgroup ends
+  wait_vmcnt<0>();
+}
+
+template <Epi EPI, bool FP8, bool PA, bool PB>
+hipError_t launch_persist(const void* a, const float* s_tok, const void* b, const float* s_ch,
+                          const uint16_t* bias, void* out, int64_t M, int64_t N, int64_t K,
+                          hipStream_t stream) {
+  const int64_t tiles_m = (M + 255) / 256;
+  const int64_t tiles_n = (N + (paired_epi(EPI) ? 127 : 255)) / (paired_epi(EPI) ? 128 : 256);
+  const int64_t tiles = tiles_m * tiles_n;
+  if ((K / 64) % 2 != 0 || K / 64 < 4 || tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const int64_t per_xcd = std::min<int64_t>((tiles + kXcds - 1) / kXcds, kCus / kXcds);
+  hipLaunchKernelGGL((gemm_persist<EPI, FP8, PA, PB>), dim3((unsigned)(per_xcd * kXcds)), dim3(256), 0, stream,
+                     static_cast<const uint8_t*>(a), s_tok, static_cast<const uint8_t*>(b), s_ch, bias, out,
+                     M, N, K, (int)tiles_m, (int)tiles_n);
+  return hipGetLastError();
+}
+
 // Tile choice.  Candidates (all 4 waves, BK = 64, 4 stages):
 //   256 x 256: waves of 128 x 128, 128 KiB LDS, one workgroup per CU;
 //   192 x 128: waves of  96 x  64,  80 KiB LDS, two per CU;
@@ -519,8 +923,14 @@ hipError_t launch_t(const void* a, const float* s_tok, const void* b, const floa
     return (double)((tiles + kCus - 1) / kCus) * bm * bn / eff;
   };
   const double c256 = cost(256, 256, 1.0), c192 = cost(192, 128, 0.90), c128 = cost(128, 128, 0.80);
-  if (c256 <= c192 && c256 <= c128)
+  if (c256 <= c192 && c256 <= c128) {
+    // persistent form: at least four stages per tile (the scale loads of a tile are
+    // waited for by its third stage) and an output a 31-bit buffer offset reaches
+    const int64_t out_bytes = M * N * (EPI == Epi::kRawI32 ? 4 : 2);
+    if (K / 64 >= 4 && out_bytes < (int64_t)kOutOfRange)
+      return launch_persist<EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
     return launch_cfg<256, 256, 2, 2, 64, 4, EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
+  }
   if (c192 <= c128)
     return launch_cfg<192, 128, 2, 2, 64, 4, EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
   return launch_cfg<128, 128, 2, 2, 64, 4, EPI, FP8, PA, PB>(a, s_tok, b, s_ch, bias, out, M, N, K, stream);
