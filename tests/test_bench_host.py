@@ -23,6 +23,9 @@ FILL = ("void at::native::vectorized_elementwise_kernel<4, at::native::FillFunct
 GEMM = ("void w8a8::(anonymous namespace)::gemm_tile<192, 128, 2, 2, 64, 4, (w8a8::Epi)1, false, true, true>"
         "(unsigned char const*, float const*, unsigned char const*, float const*, unsigned short const*, "
         "void*, long, long, long, int, int, w8a8::(anonymous namespace)::QuantOut)")
+PERSIST = ("void w8a8::(anonymous namespace)::gemm_persist<(w8a8::Epi)1, false, true, true>"
+           "(unsigned char const*, float const*, unsigned char const*, float const*, unsigned short const*, "
+           "void*, long, long, long, int, int)")
 QUANT = "void w8a8::(anonymous namespace)::quantize_rows<128, 1, true, false>(unsigned short const*, long)"
 
 
@@ -69,6 +72,18 @@ def test_pmc_summary_scales_each_counter_by_its_calibration_copy(tmp_path, monke
     assert rec["gemm_bytes_per_launch"] == pytest.approx(2000.0 * 1024 * 2 + 100.0 * 1024)
     assert rec["gemm_kernel"] == "w8a8::gemm_tile<192, 128, 2, 2, 64, 4, (w8a8::Epi)1, false, true, true>"
     assert rec["sources_digest"] == "feedfacecafebeef"
+
+
+def test_pmc_summary_finds_the_persistent_gemm(tmp_path, monkeypatch):
+    """256 x 256 workloads run gemm_persist; its dispatches are the GEMM's."""
+    monkeypatch.setattr(bench, "kernel_sources_digest", lambda: "0123456789abcdef")
+    cal_kib = bench.CALIBRATION_BYTES / 1024.0
+    _write_run(tmp_path / "f", "FETCH_SIZE", [(1, ADD, cal_kib / 2), (2, QUANT, 900.0), (3, PERSIST, 4000.0)])
+    _write_run(tmp_path / "w", "WRITE_SIZE", [(1, ADD, cal_kib), (2, QUANT, 300.0), (3, PERSIST, 250.0)])
+    rec = bench.pmc_summary("wl", str(tmp_path / "f"), str(tmp_path / "w"))
+    assert rec["gemm_kernel"] == "w8a8::gemm_persist<(w8a8::Epi)1, false, true, true>"
+    assert rec["gemm_dispatches"] == 1
+    assert rec["gemm_bytes_per_launch"] == pytest.approx(4000.0 * 1024 * 2 + 250.0 * 1024)
 
 
 def test_pmc_summary_without_a_gemm_dispatch_fails(tmp_path):
