@@ -104,18 +104,24 @@ __device__ __forceinline__ v8bf e4m3x8_to_bf16(u32x2 v) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// Block id -> (tile_m, tile_n): contiguous tile ranges per XCD, grouped along M.
-__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
-                                              int& tm, int& tn) {
-  const int q = nblocks / kXcds, r = nblocks % kXcds;
-  const int xcd = bid % kXcds, idx = bid / kXcds;
-  const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+// Tile index within the launch -> (tile_m, tile_n), walked in groups of kGroupM
+// token tiles.
+__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
   const int per_group = kGroupM * tiles_n;
   const int group = t / per_group, first_m = group * kGroupM;
   const int gsize = min(kGroupM, tiles_m - first_m);
   const int in = t % per_group;
   tm = first_m + in % gsize;
   tn = in / gsize;
+}
+
+// Block id -> (tile_m, tile_n): contiguous tile ranges per XCD, grouped along M.
+__device__ __forceinline__ void tile_of_block(int bid, int nblocks, int tiles_m, int tiles_n,
+                                              int& tm, int& tn) {
+  const int q = nblocks / kXcds, r = nblocks % kXcds;
+  const int xcd = bid % kXcds, idx = bid / kXcds;
+  const int t = (xcd < r) ? xcd * (q + 1) + idx : r * (q + 1) + (xcd - r) * q + idx;
+  tile_coords(t, tiles_m, tiles_n, tm, tn);
 }
 
 // 16 bytes from global memory straight into LDS.  The LDS address must be
@@ -530,6 +536,8 @@ hipError_t launch_cfg(const void* a, const float* s_tok, const void* b, const fl
 // scale loads were issued after the stage being waited for.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// 4 bytes per lane from global memory straight into LDS (lane i's at l + 4 i; l
+// wave-uniform).
 __device__ __forceinline__ void lds_dma4(const void* g, uint8_t* l) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
@@ -538,20 +546,12 @@ __device__ __forceinline__ void lds_dma4(const void* g, uint8_t* l) {
 
 }  // namespace
 }  // namespace w8a8
+// 16 bytes per lane to a buffer (base and size in the wave-uniform resource; a lane
+// whose offset is out of range stores nothing).
 __device__ void w8a8_raw_buffer_store_x4(w8a8::i32x4 vdata, w8a8::i32x4 rsrc, int voffset, int soffset,
                                           int aux) __asm("llvm.amdgcn.raw.buffer.store.v4i32");
 namespace w8a8 {
 namespace {
-
-// (tile index within the launch) -> (tile_m, tile_n), walked in groups of kGroupM token tiles
-__device__ __forceinline__ void tile_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int per_group = kGroupM * tiles_n;
-  const int group = t / per_group, first_m = group * kGroupM;
-  const int gsize = min(kGroupM, tiles_m - first_m);
-  const int in = t % per_group;
-  tm = first_m + in % gsize;
-  tn = in / gsize;
-}
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any persistent launch's output
 
