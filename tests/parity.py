@@ -88,3 +88,17 @@ def sample_rows(M: int, n: int = 48, seed: int = 0, tile: int = 128) -> np.ndarr
     rest = [r for r in rng.permutation(M)[: n * 2] if r not in fixed]
     rows = sorted(fixed | set(int(r) for r in rest[: max(0, n - len(fixed))]))
     return np.array(rows, dtype=np.int64)
+
+
+def tile_choice(M: int, N: int) -> str:
+    """The GEMM launcher's tile for M tokens x N weight rows (2N for gate/up): the least
+    ceil(tiles / 256) * tile area / efficiency over 256x256 (1.0), 192x128 (0.9) and
+    128x128 (0.8), ties to the larger tile.  256x256 launches run the persistent form
+    when K >= 256."""
+    def cost(bm, bn, eff):
+        tiles = -(-M // bm) * -(-N // bn)
+        return -(-tiles // 256) * bm * bn / eff
+    c256, c192, c128 = cost(256, 256, 1.0), cost(192, 128, 0.9), cost(128, 128, 0.8)
+    if c256 <= c192 and c256 <= c128:
+        return "256x256"
+    return "192x128" if c192 <= c128 else "128x128"

@@ -20,7 +20,8 @@ import pytest
 import torch
 
 import workloads as W
-from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, sample_rows, say)
+from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, sample_rows, say,
+                    tile_choice)
 
 pytestmark = pytest.mark.gpu
 
@@ -234,6 +235,31 @@ RANDOM = (_random_shapes(48, seed=2026) +
 def test_random_shapes_every_element(lib, orc, wl):
     """Seeded random shapes (ragged M, N and K, every path kind, with and without rotation),
     every element against the oracle through both weight layouts."""
+    _check_workload(lib, orc, wl)
+
+
+def _random_persistent_shapes(n, seed):
+    """Seeded shapes on which the launcher picks the 256 x 256 tile (run by the persistent
+    GEMM: several tiles per workgroup, ragged in M and N), K = 256 .. 512."""
+    rng = np.random.default_rng(seed)
+    out = []
+    while len(out) < n:
+        kind = ("linear", "gateup", "fp8")[len(out) % 3]
+        M, N, K = int(rng.integers(2600, 4200)), int(rng.integers(500, 1100)) * 8, int(rng.integers(2, 5)) * 128
+        rot, bias = int(rng.integers(0, 2)) * 128, bool(rng.integers(0, 2))
+        if tile_choice(M, 2 * N if kind == "gateup" else N) == "256x256":
+            out.append(W.custom(kind, M, K, N, rot, bias=bias, seed=seed + len(out)))
+    return out
+
+
+RANDOM_PERSISTENT = _random_persistent_shapes(6, seed=6078)
+
+
+@pytest.mark.parametrize("wl", RANDOM_PERSISTENT, ids=[w.name for w in RANDOM_PERSISTENT])
+def test_random_persistent_shapes_every_element(lib, orc, wl):
+    """Seeded random shapes that run the persistent 256 x 256 GEMM (2-5 tiles per
+    workgroup, ragged M and N, every path kind), every element against the oracle."""
+    assert tile_choice(wl.M, wl.n_w) == "256x256"
     _check_workload(lib, orc, wl)
 
 

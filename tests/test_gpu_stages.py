@@ -11,7 +11,8 @@ import pytest
 import torch
 
 import workloads as W
-from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, sample_rows, say)
+from parity import (bf16_bits, compare_bf16, compare_codes_fp8, compare_codes_i8, sample_rows, say,
+                    tile_choice as _tile_choice)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,19 +93,6 @@ def test_gemm_i32_exact(lib, orc, M, N, K):
     torch.cuda.synchronize()
     ref = orc.gemm_i32(q.numpy(), w.numpy())
     assert np.array_equal(acc.cpu().numpy(), ref)
-
-
-def _tile_choice(M, N):
-    """The launcher's tile choice for an (unpaired) GEMM of M tokens x N weight rows:
-    the least ceil(tiles / 256) * tile area / efficiency over 256x256 (1.0), 192x128
-    (0.9) and 128x128 (0.8), ties to the larger tile."""
-    def cost(bm, bn, eff):
-        tiles = -(-M // bm) * -(-N // bn)
-        return -(-tiles // 256) * bm * bn / eff
-    c256, c192, c128 = cost(256, 256, 1.0), cost(192, 128, 0.9), cost(128, 128, 0.8)
-    if c256 <= c192 and c256 <= c128:
-        return "256x256"
-    return "192x128" if c192 <= c128 else "128x128"
 
 
 # One shape per tile the launcher picks, at the workloads' depths (K = 5,120 and
