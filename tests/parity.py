@@ -94,7 +94,7 @@ def tile_choice(M: int, N: int) -> str:
     """The GEMM launcher's tile for M tokens x N weight rows (2N for gate/up): the least
     ceil(tiles / 256) * tile area / efficiency over 256x256 (1.0), 192x128 (0.9) and
     128x128 (0.8), ties to the larger tile.  256x256 launches run the persistent form
-    when K >= 256."""
+    when K >= 256 and the output is under 2^31 bytes."""
     def cost(bm, bn, eff):
         tiles = -(-M // bm) * -(-N // bn)
         return -(-tiles // 256) * bm * bn / eff

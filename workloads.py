@@ -25,6 +25,7 @@ this order, all in fp32 on the CPU:
 from __future__ import annotations
 
 from dataclasses import dataclass
+import math
 from typing import Optional
 
 import torch
@@ -148,3 +149,58 @@ def from_bits(a) -> torch.Tensor:
     """CPU bf16 tensor from a numpy uint16 array of bit patterns."""
     import numpy as np
     return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+
+
+# ------------------------------------------------------------------------------
+# Draws made directly on a device, for the cases whose tensors are too large to
+# draw on the CPU in a test's time (inputs of several GiB).  Both sides still take
+# the same tensor: the oracle reads the rows it checks back from the device.
+
+def _device_generator(seed: int, device) -> torch.Generator:
+    return torch.Generator(device=device).manual_seed(seed)
+
+
+def device_normal_bf16(rows: int, K: int, seed: int, device, outlier_frac: float = 0.01,
+                       outlier_factor: float = 20.0, sigma: float = 1.0) -> torch.Tensor:
+    """bf16 [rows, K]: N(0, 1) drawn in bf16 on ``device`` and multiplied by ``sigma``
+    (in bf16), then a seeded set of round(outlier_frac * K) columns multiplied by
+    ``outlier_factor`` (in bf16)."""
+    g = _device_generator(seed, device)
+    x = torch.randn(rows, K, generator=g, dtype=torch.bfloat16, device=device)
+    if sigma != 1.0:
+        x *= sigma
+    n_out = int(round(outlier_frac * K))
+    if n_out:
+        cols = torch.randperm(K, generator=g, device=device)[:n_out]
+        x[:, cols] *= outlier_factor
+    return x
+
+
+def device_codes(shape, seed: int, device, lo: int = -127, hi: int = 127) -> torch.Tensor:
+    """Uniform int8 codes in [lo, hi] drawn on ``device``."""
+    g = _device_generator(seed, device)
+    return torch.randint(lo, hi + 1, shape, generator=g, dtype=torch.int8, device=device)
+
+
+def device_e4m3_codes(shape, seed: int, device) -> torch.Tensor:
+    """E4M3FN code bytes (uint8) drawn on ``device``: random sign, exponent field
+    uniform in [4, 11] (magnitudes 2^-3 to 2^4 x 1.875) and mantissa field uniform in
+    [0, 7], so every code is finite and the products stay in a moderate range."""
+    g = _device_generator(seed, device)
+    sign = torch.randint(0, 2, shape, generator=g, dtype=torch.int32, device=device)
+    expo = torch.randint(4, 12, shape, generator=g, dtype=torch.int32, device=device)
+    mant = torch.randint(0, 8, shape, generator=g, dtype=torch.int32, device=device)
+    return (sign * 128 + expo * 8 + mant).to(torch.uint8)
+
+
+def device_scales(n: int, seed: int, device, lo: float = 1e-4, hi: float = 1e-1) -> torch.Tensor:
+    """Positive fp32 scales, log-uniform in [lo, hi], drawn on ``device``."""
+    g = _device_generator(seed, device)
+    u = torch.rand(n, generator=g, dtype=torch.float64, device=device)
+    return torch.exp(math.log(lo) + u * (math.log(hi) - math.log(lo))).float()
+
+
+def device_bias_bf16(n: int, seed: int, device) -> torch.Tensor:
+    """bf16 bias [n] ~ N(0, 0.01) drawn on ``device``."""
+    g = _device_generator(seed, device)
+    return (torch.randn(n, generator=g, dtype=torch.float32, device=device) * 0.01).to(torch.bfloat16)
