@@ -132,16 +132,17 @@ def kernel_sources_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per GEMM launch from the committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources; else None."""
+def stored_traffic(workload: str, kernel: str = "gemm"):
+    """HBM bytes per launch of the GEMM (or, with kernel="quantizer", of the activation
+    quantizer) from the committed rocprofv3 counter runs, if they were taken on the
+    current kernel sources; else None."""
     p = ROOT / "profiles" / f"traffic_{workload}.json"
     if not p.exists():
         return None
     rec = json.loads(p.read_text())
     if rec.get("sources_digest") != kernel_sources_digest():
         return None
-    return rec.get("gemm_bytes_per_launch")
+    return rec.get(f"{kernel}_bytes_per_launch")
 
 
 def _pmc_per_kernel(run_dir: str, counter: str):
@@ -182,12 +183,25 @@ def pmc_summary(workload: str, fetch_dir: str, write_dir: str) -> dict:
     w_factor = CALIBRATION_BYTES / (w_copy * 1024.0)
     f_gemm = sum(fetch[gemm_k]) / len(fetch[gemm_k])
     w_gemm = sum(write[gemm_k]) / len(write[gemm_k])
+
+    def short(k):
+        return k.split(">(")[0].replace("(anonymous namespace)::", "").removeprefix("void ") + ">"
     rec = {"workload": workload, "sources_digest": kernel_sources_digest(),
-           "gemm_kernel": gemm_k.split(">(")[0].replace("(anonymous namespace)::", "").removeprefix("void ") + ">", "gemm_dispatches": len(fetch[gemm_k]),
+           "gemm_kernel": short(gemm_k), "gemm_dispatches": len(fetch[gemm_k]),
            "fetch_kib_per_launch": f_gemm, "write_kib_per_launch": w_gemm,
            "copy_fetch_kib": f_copy, "copy_write_kib": w_copy,
            "fetch_factor": f_factor, "write_factor": w_factor,
            "gemm_bytes_per_launch": f_gemm * 1024.0 * f_factor + w_gemm * 1024.0 * w_factor}
+    # the activation quantizer of the same runs (the first quantizer kernel of the step;
+    # a path that also quantizes the SwiGLU output launches a second one, reported apart)
+    quant = sorted(k for k in fetch if "quantize_rows" in k and k in write)
+    for i, k in enumerate(quant):
+        f_q = sum(fetch[k]) / len(fetch[k])
+        w_q = sum(write[k]) / len(write[k])
+        tag = "quantizer" if i == 0 else f"quantizer{i + 1}"
+        rec[f"{tag}_kernel"] = short(k)
+        rec[f"{tag}_dispatches"] = len(fetch[k])
+        rec[f"{tag}_bytes_per_launch"] = f_q * 1024.0 * f_factor + w_q * 1024.0 * w_factor
     return rec
 
 
@@ -582,6 +596,7 @@ def main():
     peak = PEAK_FP8_TFLOPS if fp8 else PEAK_INT8_TOPS
     # (a stored record covers the GEMM kernel alone, not the single whole-path call)
     traffic = None if single else stored_traffic(traffic_key(wl.name, args.path))
+    q_traffic = None if single else stored_traffic(traffic_key(wl.name, args.path), "quantizer")
 
     out = {
         "metric": "W8A8 linear TOPS incl. quant+dequant, % int8 MFMA peak; quantizer GB/s",
@@ -610,7 +625,7 @@ def main():
                      "algorithmic_bytes": g_bytes},
         "quantizer": {"bound": "hbm", "achieved": q_bytes / tq / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": q_bytes / tq / 1e9 / PEAK_HBM_GBS, "avg_launch_us": tq * 1e6,
-                      "algorithmic_bytes": q_bytes},
+                      "algorithmic_bytes": q_bytes, "traffic": q_traffic},
     }
     if single:
         del out["quantizer"]

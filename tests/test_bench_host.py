@@ -83,6 +83,9 @@ def test_pmc_summary_finds_the_persistent_gemm(tmp_path, monkeypatch):
     rec = bench.pmc_summary("wl", str(tmp_path / "f"), str(tmp_path / "w"))
     assert rec["gemm_kernel"] == "w8a8::gemm_persist<(w8a8::Epi)1, false, true, true>"
     assert rec["gemm_dispatches"] == 1
+    # the quantizer of the same runs, each counter scaled by its own factor (2 and 1)
+    assert rec["quantizer_kernel"] == "w8a8::quantize_rows<128, 1, true, false>"
+    assert rec["quantizer_bytes_per_launch"] == pytest.approx((2 * 900.0 + 300.0) * 1024.0)
     assert rec["gemm_bytes_per_launch"] == pytest.approx(4000.0 * 1024 * 2 + 250.0 * 1024)
 
 
