@@ -96,6 +96,10 @@ def parse():
                     help="instead of the workload: the rate the matrix cores sustain with register "
                          "operands and no memory traffic (int8 32x32x32 and bf16 32x32x16 MFMAs), "
                          "after a ramp-up launch -- the measured-clock ceiling for the GEMM")
+    ap.add_argument("--lds-patterns", action="store_true",
+                    help="instead of the workload line: the time of the GEMM's MFMA operand reads "
+                         "from LDS (ds_read_b128 of 32 rows x 2 chunks) with no swizzle, the earlier "
+                         "swizzle key and the GEMM's key, against contiguous 16-byte reads")
     ap.add_argument("--stream-peak", action="store_true",
                     help="instead of the workload line: on each workload's activation shape, the HBM "
                          "rate of a kernel with the quantizer's traffic and no arithmetic (2 bytes read, "
@@ -324,6 +328,34 @@ def stream_peak(torch, W, lib, names, launches=50):
         torch.cuda.empty_cache()
 
 
+def lds_patterns(torch, blocks=512, iters=4096, launches=5):
+    """Per-launch time of the LDS read-pattern probe (bench-only probe library) for each
+    chunk placement, after an untimed launch of each; median of three timed runs."""
+    import statistics
+    import w8a8_quantized_linear_amd.probe as probe
+    out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    reads = blocks * 256 * 8 * iters            # ds_read_b128 per launch, lane-wise
+    rec = {"lds_patterns": {"blocks": blocks, "iters": iters, "reads_of_16_bytes": reads}}
+    for name in probe.LDS_PATTERNS:
+        probe.lds(name, iters, blocks, out)
+        torch.cuda.synchronize()
+        us = []
+        for _ in range(3):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(launches):
+                probe.lds(name, iters, blocks, out)
+            e1.record()
+            torch.cuda.synchronize()
+            us.append(e0.elapsed_time(e1) / launches * 1e3)
+        u = statistics.median(us)
+        rec[name] = {"us": u, "tb_per_s": reads * 16 / u / 1e6}
+    base = rec["contiguous"]["us"]
+    for name in probe.LDS_PATTERNS:
+        rec[name]["time_vs_contiguous"] = rec[name]["us"] / base
+    print(json.dumps(rec), flush=True)
+
+
 def vendor_gemm(torch, W, lib, names, launches=20):
     """Per-launch time of the vendor GEMM and of this library's GEMM on the same codes."""
     dev = torch.device("cuda:0")
@@ -412,6 +444,9 @@ def main():
         return
     if args.stream_peak:
         stream_peak(torch, W, lib, [n for n in W.ORDER if W.WORKLOADS[n].M >= 2048])
+        return
+    if args.lds_patterns:
+        lds_patterns(torch)
         return
     if args.drift:
         import numpy as np

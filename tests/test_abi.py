@@ -292,3 +292,7 @@ def test_probe_argument_checks():
     st = pl.w8a8_probe_stream
     assert st(2, A, A, 8, None) == -1 and st(0, None, A, 8, None) == -1 and st(1, A, None, 8, None) == -1
     assert st(0, A, A, 0, None) == -1 and st(0, A, A, -1, None) == -1
+    pl.w8a8_probe_lds.restype, pl.w8a8_probe_lds.argtypes = I, [I, I, I, P, P]
+    ld = pl.w8a8_probe_lds
+    assert ld(4, 1, 1, A, None) == -1 and ld(-1, 1, 1, A, None) == -1 and ld(0, 0, 1, A, None) == -1
+    assert ld(0, 1, 0, A, None) == -1 and ld(3, 1, 1, None, None) == -1

@@ -32,7 +32,8 @@ SOURCES = ["quantize.hip", "gemm.hip", "swiglu.hip", "short.hip", "scratch.hip",
 EXTRA = {"quantize.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 # measurement aids for the benchmark and the design tests (not the library's C ABI)
 PROBE_DIR = PKG / "probe"
-PROBE_SOURCES = ["mfma_probe.hip", "fp8_contraction.hip", "f64_mfma_layout.hip", "stream_probe.hip"]
+PROBE_SOURCES = ["mfma_probe.hip", "fp8_contraction.hip", "f64_mfma_layout.hip", "stream_probe.hip",
+                 "lds_probe.hip"]
 PROBE_LIB = PROBE_DIR / "libw8a8_probe.so"
 
 COMMON = [

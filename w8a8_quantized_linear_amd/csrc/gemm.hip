@@ -71,14 +71,16 @@ constexpr int kCus = 256;
 constexpr int kGroupM = 4;
 
 // 16-byte chunk c of LDS row r (CH chunks per row) is stored at chunk position
-// c ^ swz_key<CH>(r).  An MFMA operand read has lanes fetch the same chunk of
-// consecutive rows; the key spreads every aligned group of 8 rows over 8
-// distinct 16-byte slots modulo 128 bytes and every aligned group of 16 rows
-// over 16 distinct slots modulo 256 bytes (verified exhaustively offline).
+// c ^ swz_key<CH>(r).  An MFMA operand read (ds_read_b128) has lanes 0-31 fetch
+// chunk c of 32 consecutive rows and lanes 32-63 chunk c + 1 of the same rows.
+// With 64-byte rows the key (r ^ (r >> 2)) & 3 makes these reads conflict-free
+// on this chip's LDS: 4 cycles per read and no bank-conflict cycles, measured
+// with the LDS pattern probe and in the GEMM itself, where the earlier key
+// ((r >> 1) ^ (r >> 3)) & 3 took 8 cycles (2-way conflicts).
 template <int CH>
 __device__ __forceinline__ int swz_key(int r) {
-  if constexpr (CH == 4) return ((r >> 1) ^ (r >> 3)) & 3;
-  else return (r ^ (r >> 3)) & 7;
+  static_assert(CH == 4, "64-byte LDS rows");
+  return (r ^ (r >> 2)) & 3;
 }
 template <int CH>
 __device__ __forceinline__ int swz(int r, int c) { return (r * CH + (c ^ swz_key<CH>(r))) * 16; }

@@ -14,7 +14,9 @@ holds three kernels:
   the quantizer's rotation uses;
 * ``stream`` -- the HBM rate of a kernel with the quantizer's traffic (2 bytes read,
   1 byte written per element) and no arithmetic, or of a plain copy: the achievable
-  streaming ceiling the quantizer is set against (``bench.py --stream-peak``).
+  streaming ceiling the quantizer is set against (``bench.py --stream-peak``);
+* ``lds`` -- the cost of the GEMM's MFMA operand reads from LDS under different
+  placements of the 16-byte chunks of a row (``bench.py --lds-patterns``).
 """
 from __future__ import annotations
 
@@ -37,6 +39,8 @@ _lib.w8a8_probe_f64_mfma_layout.restype = ctypes.c_int
 _lib.w8a8_probe_f64_mfma_layout.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 _lib.w8a8_probe_stream.restype = ctypes.c_int
 _lib.w8a8_probe_stream.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
+_lib.w8a8_probe_lds.restype = ctypes.c_int
+_lib.w8a8_probe_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
 
 FP8_KINDS = {"fp8_32x32x16": 0, "f8f6f4_32x32x64": 1, "fp8_32x32x16_fp32_adds": 2, "bf16_widened": 3}
 
@@ -102,3 +106,44 @@ def stream(kind: str, x: torch.Tensor, y: torch.Tensor) -> torch.Tensor:
     if _lib.w8a8_probe_stream(k, x.data_ptr(), y.data_ptr(), x.numel() // 8, _stream()) != 0:
         raise RuntimeError("w8a8_probe_stream: bad argument or launch failure")
     return y
+
+
+LDS_PATTERNS = {"contiguous": 0, "rows_no_swizzle": 1, "rows_earlier_key": 2, "rows_gemm_key": 3}
+
+
+def lds(pattern: str, iters: int, blocks: int, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One launch of the LDS read-pattern probe on the current stream (pattern: a key
+    of LDS_PATTERNS).  Returns the int32 [blocks * 256] lane sums."""
+    k = LDS_PATTERNS[pattern]
+    if out is None:
+        out = torch.empty(blocks * 256, dtype=torch.int32, device="cuda")
+    if out.dtype != torch.int32 or not out.is_cuda or not out.is_contiguous() or out.numel() < blocks * 256:
+        raise ValueError("out: a contiguous int32 device tensor of blocks * 256 elements")
+    if _lib.w8a8_probe_lds(k, iters, blocks, out.data_ptr(), _stream()) != 0:
+        raise RuntimeError("w8a8_probe_lds: bad argument or launch failure")
+    return out
+
+
+def lds_expected(pattern: str, iters: int) -> list:
+    """Host-side value of each of the 256 lane sums of one block (the same in every
+    block): iters times the sum of the dword indices the lane reads, mod 2^32, as a
+    signed int32."""
+    k = LDS_PATTERNS[pattern]
+
+    def key(r):
+        return {2: ((r >> 1) ^ (r >> 3)) & 3, 3: (r ^ (r >> 2)) & 3}.get(k, 0)
+    sums = []
+    for tid in range(256):
+        lane, wave = tid & 63, tid >> 6
+        total = 0
+        for t in range(8):
+            if k == 0:
+                off = (t * 1024 + lane * 16) % 16384
+            else:
+                row = (wave * 64 + t * 32 + (lane & 31)) % 256
+                c = 2 * (t & 1) + (lane >> 5)
+                off = (row * 4 + (c ^ key(row))) * 16
+            total += sum(off // 4 + d for d in range(4))
+        v = (total * iters) % (1 << 32)
+        sums.append(v - (1 << 32) if v >= 1 << 31 else v)
+    return sums
