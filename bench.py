@@ -123,12 +123,12 @@ def parse():
 
 
 def kernel_sources_digest() -> str:
-    """Digest of the GEMM kernel's sources (the stored counter records are per GEMM
-    launch), with comments and blank lines removed (a comment edit does not change a
-    kernel)."""
+    """Digest of the sources of the kernels the stored counter records cover (the GEMM
+    and the activation quantizer), with comments and blank lines removed (a comment
+    edit does not change a kernel)."""
     import re
     h = hashlib.sha256()
-    for name in ("gemm.hip", "internal.h", "epilogue_math.h"):
+    for name in ("gemm.hip", "internal.h", "epilogue_math.h", "quantize.hip", "quant_math.h"):
         text = (ROOT / "w8a8_quantized_linear_amd" / "csrc" / name).read_text()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
